@@ -1,0 +1,269 @@
+"""Seeded synthetic inputs for the affine group-quantized matmul.
+
+This module only draws random tensors and lays them out in the storage
+format the library consumes. It performs none of the matmul's arithmetic:
+no unpacking, no dequantization, no accumulation. Both the HIP path and the
+CPU oracle are fed from here, so neither side can influence what the other
+one is checked on.
+
+Storage format (the contract in ``include/bitmm.h``):
+
+* bf16 tensors are ``uint16`` arrays holding the bf16 bit pattern.
+* Packed codes are ``uint32`` words along K, LSB first: code ``j`` of a word
+  occupies bits ``[bits*j, bits*(j+1))`` and word ``i`` of a row holds
+  ``k = i*(32//bits) + j``.
+* Scales and biases are bf16 ``[..., N, K // 64]``, one pair per group of 64
+  consecutive K.
+
+Workloads follow the shapes the pages measure (the mlxcel Volta pages: dense
+hidden size 5120 with a 13824-wide projection; a MoE layer of 128 experts,
+top-8 routing, expert dims 2816 / 704, 573 prompt tokens). Every draw uses
+``numpy.random.default_rng(SeedSequence([seed, tag, ...]))`` with a separate
+stream per tensor:
+
+    tag 1 = activations, 2 = codes, 3 = scales, 4 = routing, 5 = second
+    activations (MoE down-projection input)
+
+Value distributions: scale ~ U[0.001, 0.02] rounded to bf16; bias =
+-2**(bits-1) * scale (exact in bf16); codes uniform over [0, 2**bits); dense
+activations N(0, 1) (U[-1, 1] for the tiny case), rounded to bf16.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+GROUP = 64
+
+TAG_X = 1
+TAG_Q = 2
+TAG_SCALE = 3
+TAG_ROUTE = 4
+TAG_X2 = 5
+
+
+def rng_for(seed: int, tag: int, *extra: int) -> np.random.Generator:
+    """Independent generator for one tensor: SeedSequence([seed, tag, *extra])."""
+    return np.random.default_rng(np.random.SeedSequence([int(seed), int(tag), *map(int, extra)]))
+
+
+# ---------------------------------------------------------------------------
+# bf16 storage helpers (input side only)
+# ---------------------------------------------------------------------------
+
+def to_bf16_bits(a) -> np.ndarray:
+    """Round float64 values to bf16 (round to nearest, ties to even) -> uint16 bits.
+
+    Done directly from float64 (no float32 double rounding): each finite value
+    is written as r * 2**(e-8) with r an integer in [128, 256], rounded with
+    ``np.rint`` (ties to even). Inputs must be finite and inside the normal bf16
+    range, which every distribution drawn here is; zeros are allowed.
+    """
+    a = np.asarray(a, dtype=np.float64)
+    if not np.all(np.isfinite(a)):
+        raise ValueError("to_bf16_bits: non-finite input")
+    mag = np.abs(a)
+    nz = mag > 0
+    if np.any(mag[nz] < 2.0 ** -126) or np.any(mag >= 2.0 ** 128):
+        raise ValueError("to_bf16_bits: value outside the normal bf16 range")
+    m, e = np.frexp(mag)                     # mag = m * 2**e, m in [0.5, 1)
+    r = np.rint(np.ldexp(m, 8))              # integer in [128, 256]
+    carry = r == 256
+    r = np.where(carry, 128, r)
+    e = e + carry
+    expo = (e - 1 + 127).astype(np.int64)
+    if np.any(expo[nz] >= 255):
+        raise ValueError("to_bf16_bits: rounds to infinity")
+    bits = (expo << 7) | (r.astype(np.int64) - 128)
+    bits = np.where(nz, bits, 0)
+    bits = bits | np.where(np.signbit(a), 0x8000, 0)
+    return bits.astype(np.uint16)
+
+
+def bf16_bits_to_f64(bits) -> np.ndarray:
+    """Widen bf16 bit patterns (uint16) to float64 values."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
+    return b.view(np.float32).astype(np.float64)
+
+
+def pack_codes(q, bits: int) -> np.ndarray:
+    """Pack unsigned codes [..., K] into uint32 words [..., K*bits//32], LSB first."""
+    q = np.asarray(q)
+    if bits not in (4, 8):
+        raise ValueError("bits must be 4 or 8")
+    per = 32 // bits
+    if q.shape[-1] % per:
+        raise ValueError("K must be a multiple of 32/bits")
+    if q.size and (q.min() < 0 or q.max() >= (1 << bits)):
+        raise ValueError("code out of range")
+    qw = q.astype(np.uint32).reshape(*q.shape[:-1], q.shape[-1] // per, per)
+    shifts = (np.arange(per, dtype=np.uint32) * bits).astype(np.uint32)
+    return np.bitwise_or.reduce(qw << shifts, axis=-1).astype(np.uint32)
+
+
+def random_words(rng: np.random.Generator, shape) -> np.ndarray:
+    """Uniform random uint32 words: every packed code is uniform over [0, 2**bits)."""
+    return rng.integers(0, 0xFFFFFFFF, size=shape, dtype=np.uint32, endpoint=True)
+
+
+def random_scales(rng: np.random.Generator, shape) -> np.ndarray:
+    """Scales ~ U[0.001, 0.02], rounded to bf16 (uint16 bits)."""
+    return to_bf16_bits(rng.uniform(0.001, 0.02, size=shape))
+
+
+def bias_for_scales(scale_bits: np.ndarray, bits: int) -> np.ndarray:
+    """bias = -2**(bits-1) * scale; a power-of-two multiple, so exact in bf16."""
+    return to_bf16_bits(-(2.0 ** (bits - 1)) * bf16_bits_to_f64(scale_bits))
+
+
+# ---------------------------------------------------------------------------
+# Workloads
+# ---------------------------------------------------------------------------
+
+class Dense:
+    """One qmv / qmm problem: y[M,N] = x[M,K] . dequant(w)^T."""
+
+    def __init__(self, name, x, w, scales, biases, bits):
+        self.name = name
+        self.x, self.w, self.scales, self.biases = x, w, scales, biases
+        self.bits = bits
+        self.M, self.K = x.shape
+        self.N = w.shape[0]
+        assert w.shape == (self.N, self.K * bits // 32)
+        assert scales.shape == biases.shape == (self.N, self.K // GROUP)
+
+    def algorithmic_bytes(self, out_bytes: int = 2) -> int:
+        """Codes + scales + biases + x + y, each moved once."""
+        return (self.w.nbytes + self.scales.nbytes + self.biases.nbytes
+                + self.x.nbytes + self.M * self.N * out_bytes)
+
+    def flops(self) -> int:
+        return 2 * self.M * self.N * self.K
+
+
+class Gather:
+    """One expert-sorted problem: y[r,:] = x[r,:] . dequant(w[expert_idx[r]])^T."""
+
+    def __init__(self, name, x, w, scales, biases, expert_idx, bits, token_of_row=None):
+        self.name = name
+        self.x, self.w, self.scales, self.biases = x, w, scales, biases
+        self.expert_idx = expert_idx
+        self.token_of_row = token_of_row
+        self.bits = bits
+        self.B, self.K = x.shape
+        self.E, self.N = w.shape[0], w.shape[1]
+        assert w.shape == (self.E, self.N, self.K * bits // 32)
+        assert scales.shape == biases.shape == (self.E, self.N, self.K // GROUP)
+        assert expert_idx.shape == (self.B,) and expert_idx.dtype == np.int32
+
+    def algorithmic_bytes(self, out_bytes: int = 2) -> int:
+        return (self.w.nbytes + self.scales.nbytes + self.biases.nbytes + self.x.nbytes
+                + self.B * self.N * out_bytes + self.expert_idx.nbytes)
+
+    def flops(self) -> int:
+        return 2 * self.B * self.N * self.K
+
+
+def _dense_weights(seed: int, N: int, K: int, bits: int, sub: int = 0):
+    w = random_words(rng_for(seed, TAG_Q, bits, N, K, sub), (N, K * bits // 32))
+    s = random_scales(rng_for(seed, TAG_SCALE, N, K, sub), (N, K // GROUP))
+    return w, s, bias_for_scales(s, bits)
+
+
+def tiny_qmv(seed: int = 0) -> Dense:
+    """M=1, K=512, N=256, 4-bit; activations U[-1, 1]."""
+    M, K, N, bits = 1, 512, 256, 4
+    x = to_bf16_bits(rng_for(seed, TAG_X, 0).uniform(-1.0, 1.0, size=(M, K)))
+    w, s, b = _dense_weights(seed, N, K, bits, sub=0)
+    return Dense("qmv_K512_N256_b4", x, w, s, b, bits)
+
+
+_DENSE_M, _DENSE_K, _DENSE_N = 600, 5120, 13824
+
+
+def _dense_x(seed: int) -> np.ndarray:
+    return to_bf16_bits(rng_for(seed, TAG_X, 1).standard_normal(size=(_DENSE_M, _DENSE_K)))
+
+
+def hidden5120(M: int, N: int, bits: int, seed: int = 0) -> Dense:
+    """Dense problems at hidden size 5120.
+
+    All share one draw of activations [600, 5120] (M rows take the first M),
+    one draw of scales [13824, 80] and one draw of codes per bit width
+    [13824, 5120] (N columns take the first N rows of W). So the decode GEMV at
+    N=5120 sees the first 5120 output rows of the prefill weight, M=3 sees the
+    first three prefill tokens, and the 8-bit problems use identical
+    activations and scales.
+    """
+    if not (1 <= M <= _DENSE_M and 1 <= N <= _DENSE_N and bits in (4, 8)):
+        raise ValueError("hidden5120: M <= 600, N <= 13824, bits in {4, 8}")
+    x = _dense_x(seed)[:M]
+    w = random_words(rng_for(seed, TAG_Q, bits, _DENSE_N, _DENSE_K, 0),
+                     (_DENSE_N, _DENSE_K * bits // 32))[:N]
+    s = random_scales(rng_for(seed, TAG_SCALE, _DENSE_N, _DENSE_K, 0),
+                      (_DENSE_N, _DENSE_K // GROUP))[:N]
+    b = bias_for_scales(s, bits)
+    kind = "qmv" if M == 1 else "qmm"
+    return Dense(f"{kind}_M{M}_K{_DENSE_K}_N{N}_b{bits}", x, np.ascontiguousarray(w),
+                 np.ascontiguousarray(s), np.ascontiguousarray(b), bits)
+
+
+MOE_TOKENS, MOE_E, MOE_TOPK = 573, 128, 8
+MOE_HIDDEN, MOE_INTER = 2816, 704
+
+
+def moe_routing(seed: int = 0, tokens: int = MOE_TOKENS, E: int = MOE_E, top_k: int = MOE_TOPK):
+    """Each token picks top_k distinct experts uniformly; pairs flattened
+    token-major, then stable-sorted by expert. Returns (expert_idx, token_of_row)."""
+    rng = rng_for(seed, TAG_ROUTE, tokens, E, top_k)
+    choice = np.stack([rng.choice(E, top_k, replace=False) for _ in range(tokens)])
+    experts = choice.reshape(-1).astype(np.int32)
+    tokens_of = np.repeat(np.arange(tokens, dtype=np.int32), top_k)
+    order = np.argsort(experts, kind="stable")
+    return np.ascontiguousarray(experts[order]), np.ascontiguousarray(tokens_of[order])
+
+
+def moe_gather(which: str, seed: int = 0, tokens: int = MOE_TOKENS, E: int = MOE_E,
+               top_k: int = MOE_TOPK, hidden: int = MOE_HIDDEN, inter: int = MOE_INTER,
+               bits: int = 4) -> Gather:
+    """MoE prefill, expert-sorted rows.
+
+    ``which="up"``:   K=hidden, N=inter; x row r is hidden-state row token_of_row[r].
+    ``which="down"``: K=inter, N=hidden; x is a fresh N(0,1) draw [B, inter].
+    """
+    idx, tok = moe_routing(seed, tokens, E, top_k)
+    B = idx.shape[0]
+    if which == "up":
+        K, N = hidden, inter
+        h = to_bf16_bits(rng_for(seed, TAG_X, 4, tokens, hidden).standard_normal(size=(tokens, hidden)))
+        x = np.ascontiguousarray(h[tok])
+    elif which == "down":
+        K, N = inter, hidden
+        x = to_bf16_bits(rng_for(seed, TAG_X2, B, inter).standard_normal(size=(B, inter)))
+    else:
+        raise ValueError("which must be 'up' or 'down'")
+    w = random_words(rng_for(seed, TAG_Q, bits, E, N, K), (E, N, K * bits // 32))
+    s = random_scales(rng_for(seed, TAG_SCALE, E, N, K), (E, N, K // GROUP))
+    b = bias_for_scales(s, bits)
+    return Gather(f"gather_{which}_B{B}_E{E}_K{K}_N{N}_b{bits}", x, w, s, b, idx, bits, tok)
+
+
+def random_dense(M: int, N: int, K: int, bits: int, seed: int = 0, x_dist: str = "normal") -> Dense:
+    """Arbitrary-shape dense problem with the standard value distributions."""
+    rx = rng_for(seed, TAG_X, 7, M, N, K)
+    xf = rx.standard_normal(size=(M, K)) if x_dist == "normal" else rx.uniform(-1, 1, size=(M, K))
+    w, s, b = _dense_weights(seed, N, K, bits, sub=7)
+    return Dense(f"dense_M{M}_K{K}_N{N}_b{bits}", to_bf16_bits(xf), w, s, b, bits)
+
+
+def random_gather(counts, N: int, K: int, bits: int, seed: int = 0) -> Gather:
+    """Expert-sorted problem with explicit per-expert row counts (zeros allowed)."""
+    counts = np.asarray(counts, dtype=np.int64)
+    E = counts.shape[0]
+    idx = np.repeat(np.arange(E, dtype=np.int32), counts)
+    B = idx.shape[0]
+    x = to_bf16_bits(rng_for(seed, TAG_X, 8, B, N, K).standard_normal(size=(B, K)))
+    w = random_words(rng_for(seed, TAG_Q, bits, E, N, K, 8), (E, N, K * bits // 32))
+    s = random_scales(rng_for(seed, TAG_SCALE, E, N, K, 8), (E, N, K // GROUP))
+    b = bias_for_scales(s, bits)
+    return Gather(f"gather_B{B}_E{E}_K{K}_N{N}_b{bits}", x, w, s, b, idx, bits)
