@@ -1,0 +1,164 @@
+// C ABI of libbitmm (declared in include/bitmm.h): argument validation, the device
+// check, and dispatch to the kernels. Validation is pure host logic: it never
+// dereferences a pointer and makes no HIP call, so every error except
+// BITMM_ERR_DEVICE and BITMM_ERR_LAUNCH can be produced on a machine without a GPU.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <atomic>
+
+#include "../../include/bitmm.h"
+#include "kernels.hpp"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+// 0 = unknown, 1 = gfx950, 2 = other architecture.
+std::atomic<int> g_arch[kMaxDevices];
+
+// The engine's arch checks refuse a mismatched build with a named error instead of
+// an opaque load failure (issue #1538, "Baseline recorded" comment); this library is
+// built for gfx950 alone and says so the same way.
+bitmm_status device_check(hipStream_t) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+    (void)hipGetLastError();
+    return BITMM_ERR_DEVICE;
+  }
+  if (dev >= kMaxDevices) return BITMM_ERR_DEVICE;
+  int known = g_arch[dev].load(std::memory_order_relaxed);
+  if (known == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+      (void)hipGetLastError();
+      return BITMM_ERR_DEVICE;
+    }
+    known = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    g_arch[dev].store(known, std::memory_order_relaxed);
+  }
+  return known == 1 ? BITMM_OK : BITMM_ERR_DEVICE;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Shared by qmv / qmm. Sets *empty when there is nothing to compute.
+bitmm_status validate_dense(const void* x, const uint32_t* w, const void* s, const void* b,
+                            const void* y, int64_t M, int64_t N, int64_t K, int bits, int group,
+                            bitmm_out out, bool* empty) {
+  if (bits != 4 && bits != 8) return BITMM_ERR_UNSUPPORTED;
+  if (group != 64) return BITMM_ERR_UNSUPPORTED;
+  if (out != BITMM_OUT_BF16 && out != BITMM_OUT_F32) return BITMM_ERR_UNSUPPORTED;
+  if (M < 0 || N < 0 || K < 1 || K % group != 0) return BITMM_ERR_SHAPE;
+  // Index arithmetic inside the kernels is 32-bit per dimension.
+  if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX) return BITMM_ERR_SHAPE;
+  *empty = (M == 0 || N == 0);
+  if (*empty) return BITMM_OK;
+  if (!x || !w || !s || !b || !y) return BITMM_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(w, 16) || !aligned(s, 2) || !aligned(b, 2) ||
+      !aligned(y, out == BITMM_OUT_F32 ? 4 : 2))
+    return BITMM_ERR_ALIGN;
+  return BITMM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int bitmm_abi_version(void) { return BITMM_ABI_VERSION; }
+
+const char* bitmm_status_string(bitmm_status s) {
+  switch (s) {
+    case BITMM_OK: return "ok";
+    case BITMM_ERR_NULL: return "a required pointer is NULL";
+    case BITMM_ERR_SHAPE: return "invalid shape";
+    case BITMM_ERR_UNSUPPORTED: return "unsupported bits, group size or output type";
+    case BITMM_ERR_ALIGN: return "misaligned pointer";
+    case BITMM_ERR_WORKSPACE: return "workspace missing or too small";
+    case BITMM_ERR_DEVICE: return "no HIP device, or the current device is not gfx950";
+    case BITMM_ERR_LAUNCH: return "kernel launch failed";
+  }
+  return "unknown status";
+}
+
+bitmm_status bitmm_qmv(const void* x, const uint32_t* w, const void* scales, const void* biases,
+                       void* y, int64_t M, int64_t N, int64_t K, int bits, int group_size,
+                       bitmm_out out, void* stream) {
+  try {
+    bool empty = false;
+    bitmm_status st = validate_dense(x, w, scales, biases, y, M, N, K, bits, group_size, out, &empty);
+    if (st != BITMM_OK || empty) return st;
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    if ((st = device_check(hs)) != BITMM_OK) return st;
+    hipError_t e = bitmm::launch_qmv(static_cast<const uint16_t*>(x), w,
+                                     static_cast<const uint16_t*>(scales),
+                                     static_cast<const uint16_t*>(biases), y, M, N, K, bits,
+                                     out == BITMM_OUT_F32, hs);
+    return e == hipSuccess ? BITMM_OK : BITMM_ERR_LAUNCH;
+  } catch (...) {
+    return BITMM_ERR_LAUNCH;
+  }
+}
+
+bitmm_status bitmm_qmm(const void* x, const uint32_t* w, const void* scales, const void* biases,
+                       void* y, int64_t M, int64_t N, int64_t K, int bits, int group_size,
+                       bitmm_out out, void* stream) {
+  try {
+    bool empty = false;
+    bitmm_status st = validate_dense(x, w, scales, biases, y, M, N, K, bits, group_size, out, &empty);
+    if (st != BITMM_OK || empty) return st;
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    if ((st = device_check(hs)) != BITMM_OK) return st;
+    const uint16_t* xs = static_cast<const uint16_t*>(x);
+    const uint16_t* ss = static_cast<const uint16_t*>(scales);
+    const uint16_t* bs = static_cast<const uint16_t*>(biases);
+    // M*B >= 8 selects the GEMM (the engine's routing rule); below it the GEMV kernel
+    // streams W once for all rows.
+    hipError_t e = M < 8 ? bitmm::launch_qmv(xs, w, ss, bs, y, M, N, K, bits, out == BITMM_OUT_F32, hs)
+                         : bitmm::launch_qmm_mfma(xs, w, ss, bs, y, M, N, K, bits,
+                                                  out == BITMM_OUT_F32, hs);
+    return e == hipSuccess ? BITMM_OK : BITMM_ERR_LAUNCH;
+  } catch (...) {
+    return BITMM_ERR_LAUNCH;
+  }
+}
+
+size_t bitmm_gather_qmm_workspace_bytes(int64_t B, int64_t N, int64_t E) {
+  if (B < 0 || N < 0 || E < 1 || E > INT32_MAX - 2) return 0;
+  return bitmm::gather_workspace_bytes(E);
+}
+
+bitmm_status bitmm_gather_qmm(const void* x, const uint32_t* w, const void* scales,
+                              const void* biases, const int32_t* expert_idx, void* y, int64_t B,
+                              int64_t N, int64_t K, int64_t E, int bits, int group_size,
+                              bitmm_out out, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  try {
+    if (bits != 4 && bits != 8) return BITMM_ERR_UNSUPPORTED;
+    if (group_size != 64) return BITMM_ERR_UNSUPPORTED;
+    if (out != BITMM_OUT_BF16 && out != BITMM_OUT_F32) return BITMM_ERR_UNSUPPORTED;
+    if (B < 0 || N < 0 || K < 1 || E < 1 || K % group_size != 0) return BITMM_ERR_SHAPE;
+    if (B > INT32_MAX || N > INT32_MAX || K > INT32_MAX || E > INT32_MAX - 2)
+      return BITMM_ERR_SHAPE;
+    if (B == 0 || N == 0) return BITMM_OK;
+    if (!x || !w || !scales || !biases || !expert_idx || !y) return BITMM_ERR_NULL;
+    if (!workspace || workspace_bytes < bitmm_gather_qmm_workspace_bytes(B, N, E))
+      return BITMM_ERR_WORKSPACE;
+    if (!aligned(x, 16) || !aligned(w, 16) || !aligned(scales, 2) || !aligned(biases, 2) ||
+        !aligned(expert_idx, 4) || !aligned(workspace, 16) ||
+        !aligned(y, out == BITMM_OUT_F32 ? 4 : 2))
+      return BITMM_ERR_ALIGN;
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    bitmm_status st = device_check(hs);
+    if (st != BITMM_OK) return st;
+    hipError_t e = bitmm::launch_gather_qmm(
+        static_cast<const uint16_t*>(x), w, static_cast<const uint16_t*>(scales),
+        static_cast<const uint16_t*>(biases), expert_idx, y, B, N, K, E, bits,
+        out == BITMM_OUT_F32, workspace, hs);
+    return e == hipSuccess ? BITMM_OK : BITMM_ERR_LAUNCH;
+  } catch (...) {
+    return BITMM_ERR_LAUNCH;
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,164 @@
+// Expert-gathered GEMM for MoE prefill: y[r, :] = x[r, :] * dequant(w[e_r])^T with the
+// rows sorted by expert (PR #1562, section "The branch is live": the sorted-MoE fast
+// path hands a quantized GatherQMM to a grouped GEMM once the batch reaches
+// min_rows * num_experts rows, and that GEMM is preceded by one setup kernel,
+// prepare_grouped_mm_data, per launch).
+//
+// Two kernels on the caller's stream:
+//   1. prepare (one workgroup): checks the precondition (ids non-decreasing and in
+//      [0, E)), writes the status word and the per-expert row offsets into the
+//      caller's workspace.
+//   2. grouped GEMM: one workgroup per (expert, column block). It reads its expert's
+//      row range from the workspace and runs the shared matrix-core tile over those
+//      rows, so each expert's codes are streamed once per column block however many
+//      rows the expert has. Experts without rows exit at once.
+#include "kernels.hpp"
+#include "mfma_tile.hpp"
+
+namespace bitmm {
+namespace {
+
+constexpr int kPrepThreads = 1024;
+
+// ws[0]: 0 if the ids are valid, else 1 + first offending row.
+// ws[1 + e], e in [0, E]: first row whose id is >= e (row offsets of the experts).
+__global__ __launch_bounds__(kPrepThreads) void gather_prepare_kernel(const int32_t* __restrict__ idx,
+                                                                      int B, int E,
+                                                                      uint32_t* __restrict__ ws) {
+  __shared__ int first_bad;
+  if (threadIdx.x == 0) first_bad = B;
+  __syncthreads();
+  int mine = B;
+  for (int r = threadIdx.x; r < B; r += kPrepThreads) {
+    const int e = idx[r];
+    const bool bad = e < 0 || e >= E || (r > 0 && idx[r - 1] > e);
+    if (bad) {
+      mine = r;
+      break;  // rows are visited in increasing order per thread
+    }
+  }
+  if (mine < B) atomicMin(&first_bad, mine);
+  // Offsets by binary search (lower bound of e); meaningful when ids are sorted and
+  // always in bounds.
+  int32_t* off = reinterpret_cast<int32_t*>(ws + 1);
+  for (int e = threadIdx.x; e <= E; e += kPrepThreads) {
+    int lo = 0, hi = B;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (idx[mid] < e)
+        lo = mid + 1;
+      else
+        hi = mid;
+    }
+    off[e] = lo;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) ws[0] = first_bad < B ? (uint32_t)first_bad + 1u : 0u;
+}
+
+struct GatherParams {
+  const uint16_t* x;
+  const uint32_t* w;
+  const uint16_t* s;
+  const uint16_t* b;
+  void* y;
+  const uint32_t* ws;
+  int B, N, K, E;
+  int tiles_n;
+  int out_f32;
+};
+
+__device__ __forceinline__ int xcd_remap(int b, int total) {
+  if (total % 8 != 0) return b;
+  return (b % 8) * (total / 8) + b / 8;
+}
+
+template <int BITS, int MB, int NBW, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void gather_qmm_kernel(GatherParams p) {
+  using T = MmTile<BITS, MB, NBW, WAVES>;
+  __shared__ __attribute__((aligned(16))) char lds[T::LDS_BYTES];
+  // Consecutive logical ids (all column blocks of one expert) share an XCD, so the
+  // expert's activation rows are fetched into one L2.
+  const int L = xcd_remap(blockIdx.x, p.E * p.tiles_n);
+  const int e = L / p.tiles_n;
+  const int tn = L % p.tiles_n;
+  const int n0 = tn * T::BN;
+  const size_t ysz = p.out_f32 ? 4 : 2;
+
+  if (p.ws[0] != 0u) {
+    // Precondition violated: every row of y becomes zero. Workgroup (e, tn) clears
+    // rows [e*per, (e+1)*per) of its column block; together they cover all of y.
+    const int per = (p.B + p.E - 1) / p.E;
+    const int r0 = e * per;
+    const int r1 = min(p.B, r0 + per);
+    const int cols = min(T::BN, p.N - n0);
+    for (int i = threadIdx.x; i < (r1 > r0 ? (r1 - r0) * cols : 0); i += T::THREADS) {
+      const int64_t o = (int64_t)(r0 + i / cols) * p.N + n0 + i % cols;
+      if (p.out_f32)
+        static_cast<float*>(p.y)[o] = 0.f;
+      else
+        static_cast<uint16_t*>(p.y)[o] = 0;
+    }
+    return;
+  }
+  const int32_t* off = reinterpret_cast<const int32_t*>(p.ws + 1);
+  const int r_begin = off[e];
+  const int r_end = off[e + 1];
+  if (r_begin >= r_end) return;
+
+  const int64_t words = (int64_t)p.K * BITS / 32;
+  const int64_t groups = p.K / kGroup;
+  const uint32_t* we = p.w + (int64_t)e * p.N * words;
+  const uint16_t* se = p.s + (int64_t)e * p.N * groups;
+  const uint16_t* be = p.b + (int64_t)e * p.N * groups;
+  for (int r0 = r_begin; r0 < r_end; r0 += T::BM) {
+    const int rows = min(T::BM, r_end - r0);
+    T::run(p.x + (int64_t)r0 * p.K, rows, we, se, be, n0, p.N, p.K,
+           static_cast<char*>(p.y) + (size_t)r0 * p.N * ysz, p.out_f32 != 0, lds);
+    __syncthreads();  // LDS is reused by the next row block
+  }
+}
+
+template <int BITS, int MB, int NBW, int WAVES>
+hipError_t launch_grouped(GatherParams p, hipStream_t stream) {
+  using T = MmTile<BITS, MB, NBW, WAVES>;
+  p.tiles_n = (p.N + T::BN - 1) / T::BN;
+  hipLaunchKernelGGL((gather_qmm_kernel<BITS, MB, NBW, WAVES>), dim3(p.E * p.tiles_n),
+                     dim3(T::THREADS), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t gather_workspace_bytes(int64_t E) {
+  const size_t raw = (size_t)(E + 2) * sizeof(uint32_t);
+  return (raw + 255) / 256 * 256;
+}
+
+hipError_t launch_gather_qmm(const uint16_t* x, const uint32_t* w, const uint16_t* scales,
+                             const uint16_t* biases, const int32_t* expert_idx, void* y,
+                             int64_t B, int64_t N, int64_t K, int64_t E, int bits, bool out_f32,
+                             void* workspace, hipStream_t stream) {
+  uint32_t* ws = static_cast<uint32_t*>(workspace);
+  hipLaunchKernelGGL(gather_prepare_kernel, dim3(1), dim3(kPrepThreads), 0, stream, expert_idx,
+                     (int)B, (int)E, ws);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  GatherParams p;
+  p.x = x;
+  p.w = w;
+  p.s = scales;
+  p.b = biases;
+  p.y = y;
+  p.ws = ws;
+  p.B = (int)B;
+  p.N = (int)N;
+  p.K = (int)K;
+  p.E = (int)E;
+  p.tiles_n = 0;
+  p.out_f32 = out_f32 ? 1 : 0;
+  if (bits == 4) return launch_grouped<4, 4, 2, 4>(p, stream);
+  return launch_grouped<8, 4, 2, 4>(p, stream);
+}
+
+}  // namespace bitmm

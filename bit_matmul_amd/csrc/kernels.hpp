@@ -1,0 +1,28 @@
+// Internal launch interface between the C ABI (api.cpp) and the kernels.
+// Callers have validated every argument; these functions only enqueue work.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bitmm {
+
+// GEMV / small-M path: y[M, N] = x[M, K] * dequant(w)^T, rows taken 8 at a time.
+hipError_t launch_qmv(const uint16_t* x, const uint32_t* w, const uint16_t* scales,
+                      const uint16_t* biases, void* y, int64_t M, int64_t N, int64_t K, int bits,
+                      bool out_f32, hipStream_t stream);
+
+// Matrix-core GEMM for M >= 8.
+hipError_t launch_qmm_mfma(const uint16_t* x, const uint32_t* w, const uint16_t* scales,
+                           const uint16_t* biases, void* y, int64_t M, int64_t N, int64_t K,
+                           int bits, bool out_f32, hipStream_t stream);
+
+// Expert-gathered GEMM: prepare (validation + per-expert offsets into workspace),
+// then the grouped matrix-core kernel.
+size_t gather_workspace_bytes(int64_t E);
+hipError_t launch_gather_qmm(const uint16_t* x, const uint32_t* w, const uint16_t* scales,
+                             const uint16_t* biases, const int32_t* expert_idx, void* y,
+                             int64_t B, int64_t N, int64_t K, int64_t E, int bits, bool out_f32,
+                             void* workspace, hipStream_t stream);
+
+}  // namespace bitmm

@@ -1,0 +1,75 @@
+// Dense prefill GEMM on the matrix cores (M >= 8): y[M, N] = x[M, K] * dequant(w)^T.
+// The epic's kernel table puts the prefill quantized GEMM at 82% of GPU time; the
+// tile itself lives in mfma_tile.hpp.
+#include "kernels.hpp"
+#include "mfma_tile.hpp"
+
+namespace bitmm {
+namespace {
+
+struct QmmParams {
+  const uint16_t* x;
+  const uint32_t* w;
+  const uint16_t* s;
+  const uint16_t* b;
+  void* y;
+  int M, N, K;
+  int tiles_m, tiles_n;
+  int out_f32;
+};
+
+// Workgroups are dealt round-robin to the 8 XCDs, each with its own L2. Remap the
+// hardware id so every XCD gets a contiguous run of logical tiles, ordered M-fastest:
+// the M tiles that share one weight column block then run on the same XCD and read
+// its codes from that XCD's L2 instead of HBM.
+__device__ __forceinline__ int xcd_remap(int b, int total) {
+  if (total % 8 != 0) return b;
+  return (b % 8) * (total / 8) + b / 8;
+}
+
+template <int BITS, int MB, int NBW, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void qmm_mfma_kernel(QmmParams p) {
+  using T = MmTile<BITS, MB, NBW, WAVES>;
+  __shared__ __attribute__((aligned(16))) char lds[T::LDS_BYTES];
+  const int total = p.tiles_m * p.tiles_n;
+  const int L = xcd_remap(blockIdx.x, total);
+  const int tm = L % p.tiles_m;
+  const int tn = L / p.tiles_m;
+  const int m0 = tm * T::BM;
+  const int rows = min(T::BM, p.M - m0);
+  const size_t ysz = p.out_f32 ? 4 : 2;
+  T::run(p.x + (int64_t)m0 * p.K, rows, p.w, p.s, p.b, tn * T::BN, p.N, p.K,
+         static_cast<char*>(p.y) + (size_t)m0 * p.N * ysz, p.out_f32 != 0, lds);
+}
+
+template <int BITS, int MB, int NBW, int WAVES>
+hipError_t launch_tiles(QmmParams p, hipStream_t stream) {
+  using T = MmTile<BITS, MB, NBW, WAVES>;
+  p.tiles_m = (p.M + T::BM - 1) / T::BM;
+  p.tiles_n = (p.N + T::BN - 1) / T::BN;
+  hipLaunchKernelGGL((qmm_mfma_kernel<BITS, MB, NBW, WAVES>), dim3(p.tiles_m * p.tiles_n),
+                     dim3(T::THREADS), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_qmm_mfma(const uint16_t* x, const uint32_t* w, const uint16_t* scales,
+                           const uint16_t* biases, void* y, int64_t M, int64_t N, int64_t K,
+                           int bits, bool out_f32, hipStream_t stream) {
+  QmmParams p;
+  p.x = x;
+  p.w = w;
+  p.s = scales;
+  p.b = biases;
+  p.y = y;
+  p.M = (int)M;
+  p.N = (int)N;
+  p.K = (int)K;
+  p.out_f32 = out_f32 ? 1 : 0;
+  p.tiles_m = p.tiles_n = 0;
+  if (bits == 4) return launch_tiles<4, 8, 2, 4>(p, stream);
+  return launch_tiles<8, 8, 2, 4>(p, stream);
+}
+
+}  // namespace bitmm

@@ -1,0 +1,253 @@
+// GEMV / small-M kernel: y[m][n] = sum_k x[m][k] * (s[n][g] q[n][k] + b[n][g]).
+//
+// Bandwidth-bound (about 3.6 flop per byte of weights at 4 bits), so the design
+// is about the HBM stream: each wave owns RPW consecutive rows n of W; lane l
+// owns the 16-byte code chunks l, l+64, ... of every one of those rows, so a
+// wave's loads of one row cover 1 KB of contiguous memory. All CPL chunks of all
+// RPW rows are requested before any arithmetic, keeping many 128-bit loads in
+// flight per lane. The activation chunk a lane needs is the same for all RPW rows
+// and is loaded and rearranged once.
+//
+// Arithmetic: the affine split of one chunk (all of its codes share a group):
+//     sum_k x_k (s q_k + b) = s * sum_k x_k q_k + b * sum_k x_k.
+// 4-bit: a masked nibble pair OR 0x4300 is the bf16 pair (128+q_i, 128+q_{i+4}),
+// exact, so v_dot2_f32_bf16 against the matching activation pair gives
+// P = sum x (128 + q) with exact products; then s*P + (b - 128 s)*sum x.
+// 8-bit: codes convert to f32 one byte at a time and multiply f32 activations.
+// Every product is exact in f32; accumulation is f32 (the pages' decode fix,
+// epic #1536 diagnosis item 3: accumulate the 4-bit GEMV in float, not bf16).
+#pragma once
+
+#include "common.hpp"
+
+namespace bitmm {
+namespace qmv_detail {
+
+struct QmvParams {
+  const uint16_t* x;
+  const uint32_t* w;
+  const uint16_t* s;
+  const uint16_t* b;
+  void* y;
+  int N, K;
+  int out_f32;
+};
+
+constexpr int kQmvThreads = 256;
+constexpr int kQmvWaves = kQmvThreads / kWave;
+
+template <int BITS, int MR, int RPW, int CPL>
+__global__ __launch_bounds__(kQmvThreads) void qmv_kernel(QmvParams p) {
+  constexpr int CC = 128 / BITS;  // codes per 16-byte chunk
+  constexpr int XU = CC / 8;      // 16-byte activation loads per chunk and row
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = blockIdx.x * kQmvWaves + (threadIdx.x >> 6);
+  const int n0 = wave * RPW;
+  if (n0 >= p.N) return;  // uniform per wave
+  const int nch = p.K / CC;
+  const int G = p.K / kGroup;
+  const int64_t wrow = (int64_t)p.K * BITS / 32;
+
+  // Rows past N repeat the last row (loads stay in bounds); they are not stored.
+  const uint32_t* wr[RPW];
+  const uint16_t* sr[RPW];
+  const uint16_t* br[RPW];
+#pragma unroll
+  for (int r = 0; r < RPW; ++r) {
+    const int n = min(n0 + r, p.N - 1);
+    wr[r] = p.w + (int64_t)n * wrow;
+    sr[r] = p.s + (int64_t)n * G;
+    br[r] = p.b + (int64_t)n * G;
+  }
+
+  float acc[RPW][MR];
+#pragma unroll
+  for (int r = 0; r < RPW; ++r)
+#pragma unroll
+    for (int m = 0; m < MR; ++m) acc[r][m] = 0.f;
+
+  for (int kb = 0; kb < nch; kb += kWave * CPL) {
+    // 1. Weight stream: every chunk of every row, up front.
+    u32x4_t q[CPL][RPW];
+    float sv[CPL][RPW], bv[CPL][RPW];
+    bool ok[CPL];
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+      const int c = kb + i * kWave + lane;
+      ok[i] = c < nch;
+      const int cc = ok[i] ? c : 0;
+      const int g = cc * CC / kGroup;
+#pragma unroll
+      for (int r = 0; r < RPW; ++r) {
+        q[i][r] = load_stream(wr[r] + 4 * (int64_t)cc);
+        sv[i][r] = bf16_to_f32(sr[r][g]);
+        bv[i][r] = bf16_to_f32(br[r][g]);
+      }
+    }
+    // 2. Activations for the same chunks (L1/L2 resident, shared by all waves).
+    u32x4_t xr[CPL][MR][XU];
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+      const int cc = ok[i] ? kb + i * kWave + lane : 0;
+#pragma unroll
+      for (int m = 0; m < MR; ++m) {
+        const uint16_t* xp = p.x + (int64_t)m * p.K + (int64_t)cc * CC;
+#pragma unroll
+        for (int u = 0; u < XU; ++u) {
+          const u32x4_t v = load_u128(xp + 8 * u);
+          xr[i][m][u] = ok[i] ? v : u32x4_t{0u, 0u, 0u, 0u};
+        }
+      }
+    }
+    // 3. Arithmetic.
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+      if constexpr (BITS == 4) {
+        // Activation pairs matching the nibble pairs (i, i+4) of each word.
+        uint32_t xp[MR][4][4];
+        float sx[MR];
+#pragma unroll
+        for (int m = 0; m < MR; ++m) {
+          const uint32_t* xd = reinterpret_cast<const uint32_t*>(&xr[i][m][0]);
+          float t = 0.f;
+#pragma unroll
+          for (int wd = 0; wd < 4; ++wd) {
+            const uint32_t d0 = xd[4 * wd + 0], d1 = xd[4 * wd + 1];
+            const uint32_t d2 = xd[4 * wd + 2], d3 = xd[4 * wd + 3];
+            xp[m][wd][0] = perm_b32(d2, d0, 0x05040100u);  // (x0, x4)
+            xp[m][wd][1] = perm_b32(d2, d0, 0x07060302u);  // (x1, x5)
+            xp[m][wd][2] = perm_b32(d3, d1, 0x05040100u);  // (x2, x6)
+            xp[m][wd][3] = perm_b32(d3, d1, 0x07060302u);  // (x3, x7)
+            t = dot2_bf16(d0, 0x3F803F80u, t);
+            t = dot2_bf16(d1, 0x3F803F80u, t);
+            t = dot2_bf16(d2, 0x3F803F80u, t);
+            t = dot2_bf16(d3, 0x3F803F80u, t);
+          }
+          sx[m] = t;
+        }
+#pragma unroll
+        for (int r = 0; r < RPW; ++r) {
+          const uint32_t wq[4] = {q[i][r][0], q[i][r][1], q[i][r][2], q[i][r][3]};
+          float P[MR];
+#pragma unroll
+          for (int m = 0; m < MR; ++m) P[m] = 0.f;
+#pragma unroll
+          for (int wd = 0; wd < 4; ++wd) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const uint32_t qp = ((wq[wd] >> (4 * j)) & 0x000F000Fu) | 0x43004300u;
+#pragma unroll
+              for (int m = 0; m < MR; ++m) P[m] = dot2_bf16(qp, xp[m][wd][j], P[m]);
+            }
+          }
+          const float s = sv[i][r];
+          const float cb = fmaf(-128.f, s, bv[i][r]);
+#pragma unroll
+          for (int m = 0; m < MR; ++m) acc[r][m] = fmaf(s, P[m], fmaf(cb, sx[m], acc[r][m]));
+        }
+      } else {
+        float xf[MR][16];
+        float sx[MR];
+#pragma unroll
+        for (int m = 0; m < MR; ++m) {
+          const uint32_t* xd = reinterpret_cast<const uint32_t*>(&xr[i][m][0]);
+          float t = 0.f;
+#pragma unroll
+          for (int d = 0; d < 8; ++d) {
+            xf[m][2 * d] = bf16_lo(xd[d]);
+            xf[m][2 * d + 1] = bf16_hi(xd[d]);
+            t += xf[m][2 * d];
+            t += xf[m][2 * d + 1];
+          }
+          sx[m] = t;
+        }
+#pragma unroll
+        for (int r = 0; r < RPW; ++r) {
+          const uint32_t wq[4] = {q[i][r][0], q[i][r][1], q[i][r][2], q[i][r][3]};
+          float P[MR];
+#pragma unroll
+          for (int m = 0; m < MR; ++m) P[m] = 0.f;
+#pragma unroll
+          for (int wd = 0; wd < 4; ++wd) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const float qf = (float)((wq[wd] >> (8 * j)) & 0xFFu);
+#pragma unroll
+              for (int m = 0; m < MR; ++m) P[m] = fmaf(xf[m][4 * wd + j], qf, P[m]);
+            }
+          }
+          const float s = sv[i][r];
+          const float b = bv[i][r];
+#pragma unroll
+          for (int m = 0; m < MR; ++m) acc[r][m] = fmaf(s, P[m], fmaf(b, sx[m], acc[r][m]));
+        }
+      }
+    }
+  }
+
+  // 4. Wave reductions; lane 0 stores.
+#pragma unroll
+  for (int r = 0; r < RPW; ++r) {
+#pragma unroll
+    for (int m = 0; m < MR; ++m) {
+      const float v = wave_sum(acc[r][m]);
+      const int n = n0 + r;
+      if (lane == 0 && n < p.N) {
+        const int64_t o = (int64_t)m * p.N + n;
+        if (p.out_f32)
+          static_cast<float*>(p.y)[o] = v;
+        else
+          static_cast<uint16_t*>(p.y)[o] = f32_to_bf16(v);
+      }
+    }
+  }
+}
+
+template <int BITS, int MR, int RPW, int CPL>
+hipError_t launch_one(const QmvParams& p, hipStream_t stream) {
+  const int waves = (p.N + RPW - 1) / RPW;
+  const int blocks = (waves + kQmvWaves - 1) / kQmvWaves;
+  hipLaunchKernelGGL((qmv_kernel<BITS, MR, RPW, CPL>), dim3(blocks), dim3(kQmvThreads), 0, stream,
+                     p);
+  return hipGetLastError();
+}
+
+// Rows of W per wave: more rows share one activation load; fewer rows give more
+// waves (and more loads in flight) when N is small.
+template <int BITS, int MR, int CPL>
+hipError_t pick_rpw(const QmvParams& p, hipStream_t stream) {
+  constexpr int RPW = MR <= 2 ? 4 : 2;
+  return launch_one<BITS, MR, RPW, CPL>(p, stream);
+}
+
+template <int BITS, int MR>
+hipError_t pick_cpl(const QmvParams& p, int cpl, hipStream_t stream) {
+  switch (cpl) {
+    case 1: return pick_rpw<BITS, MR, 1>(p, stream);
+    case 2: return pick_rpw<BITS, MR, 2>(p, stream);
+    case 3: return pick_rpw<BITS, MR, 3>(p, stream);
+    default: return pick_rpw<BITS, MR, 4>(p, stream);
+  }
+}
+
+template <int BITS>
+hipError_t launch_bits(const QmvParams& p, int mr, int cpl, hipStream_t stream) {
+  switch (mr) {
+    case 1: return pick_cpl<BITS, 1>(p, cpl, stream);
+    case 2: return pick_cpl<BITS, 2>(p, cpl, stream);
+    case 3: return pick_cpl<BITS, 3>(p, cpl, stream);
+    case 4: return pick_cpl<BITS, 4>(p, cpl, stream);
+    case 5: return pick_cpl<BITS, 5>(p, cpl, stream);
+    case 6: return pick_cpl<BITS, 6>(p, cpl, stream);
+    case 7: return pick_cpl<BITS, 7>(p, cpl, stream);
+    default: return pick_cpl<BITS, 8>(p, cpl, stream);
+  }
+}
+
+}  // namespace qmv_detail
+
+// One explicit instantiation per bit width, each in its own translation unit.
+extern template hipError_t qmv_detail::launch_bits<4>(const qmv_detail::QmvParams&, int, int, hipStream_t);
+extern template hipError_t qmv_detail::launch_bits<8>(const qmv_detail::QmvParams&, int, int, hipStream_t);
+
+}  // namespace bitmm

@@ -1,0 +1,133 @@
+/*
+ * bitmm: affine group-wise quantized matrix multiply on AMD Instinct MI355X (gfx950).
+ *
+ * The operation. The epic "NVIDIA Volta (sm_70) inference acceleration program"
+ * (mlxcel #1536) profiles an inference engine whose GPU time is dominated by two
+ * quantized-weight kernels: the prefill GEMM (its kernel table's first row) and
+ * the decode GEMV (second row). Its Baseline section describes the weights as
+ * affine quantized, 4-bit codes in groups of 64, with every other tensor in bf16;
+ * issue #1538 ("Volta (sm_70) baseline record and build coverage", comments of
+ * 2026-08-31) adds 8-bit codes. PR #1562 ("tag the pre-Ampere grouped GEMM arm
+ * Sm70, not Sm75", section "The branch is live") adds the third form: the
+ * quantized GatherQMM that a MoE prefill runs over rows sorted by expert. All
+ * three compute
+ *
+ *     y[r][n] = sum_k x[r][k] * w[e_r][n][k],
+ *     w[e][n][k] = s[e][n][k/64] * q[e][n][k] + b[e][n][k/64],
+ *
+ * with e_r = 0 for the dense forms and e_r = expert_idx[r] for the gathered one.
+ *
+ * Storage (all row-major, contiguous, little-endian):
+ *   x        bf16 [M, K]                 (activations; bf16 passed as uint16 bits)
+ *   w        uint32 [E, N, K*bits/32]    (codes along K, LSB first: code j of a word
+ *                                         sits in bits [bits*j, bits*(j+1)) and word i
+ *                                         of a row holds k = i*(32/bits) + j)
+ *   scales   bf16 [E, N, K/64]           (one scale per row n and group of 64 along K)
+ *   biases   bf16 [E, N, K/64]
+ *   y        bf16 or f32 [M, N]          (bf16 rounded to nearest even from f32)
+ * Dense calls have E = 1 and no leading E dimension.
+ *
+ * Precision. Accumulation is always f32 (the pages' decode fix, PR #1539 in the
+ * epic's sub-issue list, is to stop accumulating the 4-bit GEMV in bf16).
+ *   - bitmm_qmv, and bitmm_qmm for M < 8: every product x*w is formed exactly (the
+ *     code enters as an exact bf16 integer and the group scale is applied in f32).
+ *   - bitmm_qmm for M >= 8 and bitmm_gather_qmm: w = fma(s, q, b) in f32 is rounded
+ *     to bf16 and multiplied on the matrix cores (a dense bf16 GEMM after
+ *     dequantization, as the grouped path on the pages is), f32 accumulate.
+ *
+ * Conventions.
+ *   - Pointers are DEVICE pointers owned by the caller; nothing is retained after
+ *     the call returns and the library allocates no memory.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream) and the
+ *     call returns without synchronising. Calls are re-entrant and may run
+ *     concurrently on different streams. Results are bitwise deterministic.
+ *   - Arguments are validated on the host before any HIP call; a validation error
+ *     enqueues nothing. M = 0, N = 0 or B = 0 is a valid empty problem (BITMM_OK,
+ *     nothing enqueued, pointers unused).
+ *   - No C++ exception crosses this interface.
+ */
+#ifndef BITMM_H
+#define BITMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BITMM_ABI_VERSION 1
+
+typedef enum {
+  BITMM_OK = 0,
+  BITMM_ERR_NULL = 1,        /* a required pointer is NULL                                  */
+  BITMM_ERR_SHAPE = 2,       /* M, N, B < 0; K < 1; E < 1; or K % group_size != 0           */
+  BITMM_ERR_UNSUPPORTED = 3, /* bits not in {4, 8}; group_size != 64; unknown output type   */
+  BITMM_ERR_ALIGN = 4,       /* x, w or workspace not 16-byte aligned; scales or biases not
+                                2-byte aligned; y not aligned to its element size;
+                                expert_idx not 4-byte aligned                               */
+  BITMM_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than bitmm_gather_qmm_workspace_bytes */
+  BITMM_ERR_DEVICE = 6,      /* no HIP device, or the current device is not gfx950          */
+  BITMM_ERR_LAUNCH = 7       /* a kernel launch reported an error                           */
+} bitmm_status;
+
+typedef enum { BITMM_OUT_BF16 = 0, BITMM_OUT_F32 = 1 } bitmm_out;
+
+/* Version of this interface (BITMM_ABI_VERSION). */
+int bitmm_abi_version(void);
+
+/* Static, human-readable name of a status code ("unknown status" otherwise). */
+const char* bitmm_status_string(bitmm_status s);
+
+/*
+ * Decode GEMV: y[M, N] = x[M, K] * dequant(w)^T, streaming W once per call for all M
+ * rows (rows are taken eight at a time). Meant for M = 1 (the decode step the epic's
+ * kernel table lists second); any M >= 0 is accepted.
+ *   x: bf16 [M, K]; w: uint32 [N, K*bits/32]; scales, biases: bf16 [N, K/group_size];
+ *   y: [M, N] of type `out`. bits in {4, 8}; group_size == 64; K a multiple of 64.
+ */
+bitmm_status bitmm_qmv(const void* x, const uint32_t* w, const void* scales, const void* biases,
+                       void* y, int64_t M, int64_t N, int64_t K, int bits, int group_size,
+                       bitmm_out out, void* stream);
+
+/*
+ * Prefill GEMM: same operation and arguments as bitmm_qmv, for any M. Following the
+ * engine's routing rule quoted in issue #1538 (the first 2026-08-31 comment: M*B >= 8
+ * selects the GEMM), M < 8 runs the GEMV kernel (the small-M path) and M >= 8 the
+ * matrix-core kernel.
+ */
+bitmm_status bitmm_qmm(const void* x, const uint32_t* w, const void* scales, const void* biases,
+                       void* y, int64_t M, int64_t N, int64_t K, int bits, int group_size,
+                       bitmm_out out, void* stream);
+
+/*
+ * Bytes of device workspace bitmm_gather_qmm needs for B rows, N columns and E experts
+ * (a multiple of 256; 0 if an argument is negative or E < 1).
+ */
+size_t bitmm_gather_qmm_workspace_bytes(int64_t B, int64_t N, int64_t E);
+
+/*
+ * Expert-gathered GEMM (MoE prefill over rows sorted by expert; PR #1562):
+ *   y[r, :] = x[r, :] * dequant(w[expert_idx[r]])^T for r in [0, B)
+ *   x: bf16 [B, K]; w: uint32 [E, N, K*bits/32]; scales, biases: bf16 [E, N, K/group_size];
+ *   expert_idx: int32 [B]; y: [B, N] of type `out`.
+ * PRECONDITION: expert_idx is non-decreasing with every value in [0, E). This is checked
+ * on the device: word 0 (uint32) of `workspace` receives 0 if it holds, otherwise 1 + the
+ * first offending row, and then every row of y is written as zeros. Words 1..E+1 receive
+ * the row offset of each expert (int32; expert e owns rows [off[e], off[e+1])). The caller
+ * may read them back once the stream has reached this call; the library never waits.
+ * `workspace` is caller-owned device memory of at least
+ * bitmm_gather_qmm_workspace_bytes(B, N, E) bytes, 16-byte aligned; it needs no
+ * initialisation. Two calls sharing one workspace must be ordered on one stream.
+ */
+bitmm_status bitmm_gather_qmm(const void* x, const uint32_t* w, const void* scales,
+                              const void* biases, const int32_t* expert_idx, void* y, int64_t B,
+                              int64_t N, int64_t K, int64_t E, int bits, int group_size,
+                              bitmm_out out, void* workspace, size_t workspace_bytes,
+                              void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BITMM_H */

@@ -1,0 +1,297 @@
+"""GPU parity: the HIP kernels, called through the C ABI, against the CPU oracle.
+
+Small problems are compared on every output; the full-size workloads (decode GEMV
+at hidden 5120, prefill GEMM M=600 and M=3, their 8-bit twins, the MoE gather in
+both orientations) on sampled outputs the oracle computes one by one, plus
+properties that hold at any size (finite, deterministic). Integer-valued inputs
+must match exactly; the constant-per-expert case exposes any mis-gathered row.
+"""
+
+import numpy as np
+import pytest
+
+import bit_matmul_amd as bm
+import oracle
+from bit_matmul_amd import inputs as I
+from tests import gpu_util as G
+from tests.pins import integer_exact_problem
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    t = G.torch()
+    if not t.cuda.is_available():
+        pytest.skip("no GPU")
+    bm.lib()
+    yield
+    t.cuda.synchronize()
+
+
+def oracle_dense(d):
+    return oracle.qmm(d.x, d.w, d.scales, d.biases, d.bits)
+
+
+# ---------------------------------------------------------------------------
+# Small problems: every output
+# ---------------------------------------------------------------------------
+
+QMV_SHAPES = [(1, 1, 64), (1, 256, 512), (1, 300, 640), (1, 257, 192), (1, 64, 8192 + 64),
+              (2, 77, 320), (3, 133, 5120), (5, 40, 576), (7, 19, 128), (8, 33, 256),
+              (11, 50, 192)]
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("out", ["bf16", "f32"])
+@pytest.mark.parametrize("M,N,K", QMV_SHAPES)
+def test_qmv_small(M, N, K, bits, out):
+    d = I.random_dense(M, N, K, bits, seed=M + N + K)
+    got = G.to_f64(G.run_dense("bitmm_qmv", d, out))
+    G.assert_close(got, oracle_dense(d), out, f"qmv M{M} N{N} K{K} b{bits}")
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("out", ["bf16", "f32"])
+@pytest.mark.parametrize("M,N,K", [(1, 130, 320), (2, 64, 128), (3, 200, 640), (5, 33, 192),
+                                   (7, 129, 1024)])
+def test_qmm_small_m(M, N, K, bits, out):
+    d = I.random_dense(M, N, K, bits, seed=7 * M + N + K)
+    got = G.to_f64(G.run_dense("bitmm_qmm", d, out))
+    G.assert_close(got, oracle_dense(d), out, f"qmm-smallM M{M} N{N} K{K} b{bits}")
+
+
+MFMA_SHAPES = [(8, 16, 64), (9, 100, 192), (16, 128, 128), (33, 70, 320), (130, 300, 576),
+               (129, 257, 1024), (257, 129, 192), (200, 513, 448)]
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("out", ["bf16", "f32"])
+@pytest.mark.parametrize("M,N,K", MFMA_SHAPES)
+def test_qmm_mfma_small(M, N, K, bits, out):
+    d = I.random_dense(M, N, K, bits, seed=3 * M + N + K)
+    got = G.to_f64(G.run_dense("bitmm_qmm", d, out))
+    # The matrix-core path rounds w to bf16 before the product, so it is held to the
+    # bf16 rule for both output types.
+    G.assert_close(got, oracle_dense(d), "bf16", f"qmm-mfma M{M} N{N} K{K} b{bits} {out}")
+
+
+GATHER_COUNTS = [
+    [5, 0, 3, 17, 1, 0, 64, 70, 2],      # empty experts, one > 64 rows
+    [1],                                  # one expert, one row
+    [0, 0, 9],                            # leading empty experts
+    [40] * 6,
+    [3, 129, 0, 1],                       # a segment spanning three row blocks
+]
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("out", ["bf16", "f32"])
+@pytest.mark.parametrize("ci", range(len(GATHER_COUNTS)))
+@pytest.mark.parametrize("N,K", [(200, 192), (64, 576), (129, 128)])
+def test_gather_small(ci, N, K, bits, out):
+    g = I.random_gather(GATHER_COUNTS[ci], N=N, K=K, bits=bits, seed=ci + N + K)
+    y, ws = G.run_gather(g, out)
+    ref = oracle.gather_qmm(g.x, g.w, g.scales, g.biases, g.expert_idx, bits)
+    G.assert_close(G.to_f64(y), ref, "bf16", f"gather {GATHER_COUNTS[ci]} N{N} K{K} b{bits}")
+    w = ws.cpu().numpy().view(np.uint32)
+    assert w[0] == 0
+    exp_off = np.searchsorted(g.expert_idx, np.arange(g.E + 1), side="left")
+    assert np.array_equal(w[1:g.E + 2].view(np.int32), exp_off)
+
+
+# ---------------------------------------------------------------------------
+# Exact cases
+# ---------------------------------------------------------------------------
+
+def _exact_dense(M, N, K, bits, seed):
+    x, w, s, b, y4 = integer_exact_problem(M, N, K, bits, seed)
+    d = I.Dense("exact", x, w, s, b, bits)
+    return d, y4.astype(np.float64) / 4.0
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("fn,M,N,K", [("bitmm_qmv", 1, 300, 5120), ("bitmm_qmm", 3, 257, 5120),
+                                      ("bitmm_qmm", 64, 300, 5120), ("bitmm_qmm", 130, 129, 192)])
+def test_integer_exact(fn, M, N, K, bits):
+    """Every weight, product and partial sum is exact in f32: outputs must match the
+    exact result bit for bit (f32) and its round-to-nearest-even bf16 (bf16)."""
+    d, exact = _exact_dense(M, N, K, bits, seed=M * N + bits)
+    assert np.array_equal(oracle_dense(d), exact)
+    got32 = G.to_f64(G.run_dense(fn, d, "f32"))
+    assert np.array_equal(got32, exact), np.max(np.abs(got32 - exact))
+    got16 = G.run_dense(fn, d, "bf16")
+    t = G.torch()
+    bits16 = got16.view(t.int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(bits16, oracle.f64_to_bf16(exact))
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_gather_integer_exact(bits):
+    counts = [7, 0, 30, 66, 1]
+    N, K = 90, 2816
+    E = len(counts)
+    idx = np.repeat(np.arange(E, dtype=np.int32), counts)
+    B = idx.size
+    rng = np.random.default_rng(bits)
+    xi = rng.integers(-2, 3, size=(B, K))
+    q = rng.integers(0, 1 << bits, size=(E, N, K))
+    s4 = rng.choice([1, 2, 4, 8], size=(E, N, K // 64))
+    half = 1 << (bits - 1)
+    g = I.Gather("exact", I.to_bf16_bits(xi.astype(np.float64)), I.pack_codes(q, bits),
+                 I.to_bf16_bits(s4 / 4.0), I.to_bf16_bits(-half * s4 / 4.0), idx, bits)
+    exact = np.empty((B, N))
+    for e in range(E):
+        rows = idx == e
+        w4 = np.repeat(s4[e], 64, axis=1) * (q[e] - half)
+        exact[rows] = (xi[rows].astype(np.int64) @ w4.T.astype(np.int64)) / 4.0
+    assert np.array_equal(oracle.gather_qmm(g.x, g.w, g.scales, g.biases, idx, bits), exact)
+    y, _ = G.run_gather(g, "f32")
+    assert np.array_equal(G.to_f64(y), exact)
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_constant_per_expert(bits):
+    """q = 0, b[e] = e + 1, x[r,:] = (r mod 7) + 1: y[r,n] = K (e_r + 1)((r mod 7) + 1)."""
+    counts = [3, 0, 50, 1, 0, 70, 9, 2]
+    E, N, K = len(counts), 150, 704
+    idx = np.repeat(np.arange(E, dtype=np.int32), counts)
+    B = idx.size
+    w = np.zeros((E, N, K * bits // 32), dtype=np.uint32)
+    s = I.to_bf16_bits(np.full((E, N, K // 64), 0.5))
+    b = I.to_bf16_bits(np.broadcast_to((np.arange(E) + 1.0)[:, None, None], (E, N, K // 64)))
+    xv = (np.arange(B) % 7 + 1).astype(np.float64)
+    x = I.to_bf16_bits(np.broadcast_to(xv[:, None], (B, K)))
+    g = I.Gather("const", x, w, s, b, idx, bits)
+    exp = K * (idx[:, None] + 1.0) * xv[:, None] * np.ones((1, N))
+    y, _ = G.run_gather(g, "f32")
+    assert np.array_equal(G.to_f64(y), exp)
+
+
+# ---------------------------------------------------------------------------
+# Precondition violations and degenerate inputs
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("kind,row", [("unsorted", 5), ("negative", 0), ("too_large", 11)])
+def test_gather_violation_flag(kind, row):
+    g = I.random_gather([4, 4, 4], N=70, K=128, bits=4, seed=1)
+    idx = g.expert_idx.copy()
+    if kind == "unsorted":
+        idx[row] = 0           # 1 after a 1 ... -> 0 breaks the order at row 5
+    elif kind == "negative":
+        idx[row] = -1
+    else:
+        idx[row] = 3           # E = 3
+    y, ws = G.run_gather(g, "bf16", idx=idx)
+    flag = int(ws[:4].cpu().numpy().view(np.uint32)[0])
+    assert flag == row + 1
+    assert np.all(G.to_f64(y) == 0.0)
+
+
+def test_empty_problems():
+    t = G.torch()
+    x = t.empty((0, 128), dtype=t.bfloat16, device=G.dev())
+    w = t.zeros((16, 16), dtype=t.int32, device=G.dev())
+    s = t.zeros((16, 2), dtype=t.bfloat16, device=G.dev())
+    y = t.empty((0, 16), dtype=t.bfloat16, device=G.dev())
+    bm.bitmm_qmv(x, w, s, s, y, 4)
+    bm.bitmm_qmm(x, w, s, s, y, 4)
+    g = I.random_gather([0, 0], N=16, K=128, bits=4)
+    yg, _ = G.run_gather(g, "bf16")
+    assert yg.shape == (0, 16)
+
+
+# ---------------------------------------------------------------------------
+# Full-size workloads: sampled outputs, in the configuration the benchmark times
+# ---------------------------------------------------------------------------
+
+FULL_DENSE = [(1, 5120, 4), (1, 13824, 4), (600, 13824, 4), (3, 13824, 4),
+              (1, 5120, 8), (1, 13824, 8), (600, 13824, 8), (3, 13824, 8)]
+
+
+def test_tiny_qmv_full():
+    d = I.tiny_qmv()
+    for out in ("bf16", "f32"):
+        got = G.to_f64(G.run_dense("bitmm_qmv", d, out))
+        G.assert_close(got, oracle_dense(d), out, f"tiny qmv {out}")
+
+
+@pytest.mark.parametrize("M,N,bits", FULL_DENSE)
+def test_hidden5120_sampled(M, N, bits):
+    d = I.hidden5120(M, N, bits)
+    fn = "bitmm_qmv" if M == 1 else "bitmm_qmm"
+    exact_path = M < 8
+    for out in (("bf16", "f32") if exact_path else ("bf16",)):
+        y = G.run_dense(fn, d, out)
+        y2 = G.run_dense(fn, d, out)
+        t = G.torch()
+        assert t.equal(y, y2), "not deterministic"
+        got = G.to_f64(y)
+        assert np.all(np.isfinite(got))
+        r, c = G.sample_points(d.M, d.N, 3000, seed=M + N)
+        ref = oracle.qmm_points(d.x, d.w, d.scales, d.biases, r, c, bits)
+        G.assert_close(got[r, c], ref, out, f"{d.name} {out}")
+
+
+@pytest.mark.parametrize("which", ["up", "down"])
+def test_moe_gather_sampled(which):
+    g = I.moe_gather(which)
+    y, ws = G.run_gather(g, "bf16")
+    y2, _ = G.run_gather(g, "bf16")
+    t = G.torch()
+    assert t.equal(y, y2)
+    wsn = ws.cpu().numpy().view(np.uint32)
+    assert wsn[0] == 0
+    got = G.to_f64(y)
+    r, c = G.sample_points(g.B, g.N, 3000, seed=5)
+    ref = oracle.gather_qmm_points(g.x, g.w, g.scales, g.biases, g.expert_idx, r, c, g.bits)
+    G.assert_close(got[r, c], ref, "bf16", g.name)
+
+
+# ---------------------------------------------------------------------------
+# Determinism, streams, cross-op consistency
+# ---------------------------------------------------------------------------
+
+def test_repeat_bitwise_identical():
+    t = G.torch()
+    d = I.random_dense(1, 777, 2048, 4, seed=9)
+    m = I.random_dense(96, 300, 1024, 8, seed=10)
+    g = I.random_gather([20, 0, 50, 7], N=160, K=384, bits=4, seed=11)
+    for _ in range(2):
+        a = [G.run_dense("bitmm_qmv", d) for _ in range(10)]
+        b = [G.run_dense("bitmm_qmm", m) for _ in range(10)]
+        c = [G.run_gather(g)[0] for _ in range(10)]
+        for seq in (a, b, c):
+            for v in seq[1:]:
+                assert t.equal(v, seq[0])
+
+
+def test_side_stream_matches_default():
+    t = G.torch()
+    d = I.random_dense(130, 300, 640, 4, seed=12)
+    ref = G.run_dense("bitmm_qmm", d)
+    s1, s2 = t.cuda.Stream(), t.cuda.Stream()
+    with t.cuda.stream(s1):
+        y1 = G.run_dense("bitmm_qmm", d, stream=s1)
+    with t.cuda.stream(s2):
+        y2 = G.run_dense("bitmm_qmm", d, stream=s2)
+    t.cuda.synchronize()
+    assert t.equal(y1, ref) and t.equal(y2, ref)
+
+
+def test_cross_op_consistency():
+    """qmm at M=1 is the GEMV; the first rows of an M=600 GEMM agree with M=3;
+    a single-expert gather agrees with qmm."""
+    t = G.torch()
+    d1 = I.random_dense(1, 500, 1024, 4, seed=13)
+    assert t.equal(G.run_dense("bitmm_qmv", d1), G.run_dense("bitmm_qmm", d1))
+    big = I.hidden5120(64, 2048, 4)
+    small = I.Dense("first3", big.x[:3].copy(), big.w, big.scales, big.biases, 4)
+    yb = G.to_f64(G.run_dense("bitmm_qmm", big, "f32"))[:3]
+    ys = G.to_f64(G.run_dense("bitmm_qmm", small, "f32"))
+    G.assert_close(yb, ys, "bf16", "M=64 rows 0-2 vs M=3")
+    g = I.random_gather([300], N=200, K=512, bits=8, seed=14)
+    dg = I.Dense("e0", g.x, g.w[0], g.scales[0], g.biases[0], 8)
+    yg, _ = G.run_gather(g, "f32")
+    ym = G.run_dense("bitmm_qmm", dg, "f32")
+    assert t.equal(yg, ym)
