@@ -11,9 +11,10 @@ tensors (copies rotate through more than 1 GiB), so the 256 MB Infinity Cache an
 the 4 MB L2s cannot serve them: every step streams its weights from HBM, as a
 decode step does when every layer has its own weights.
 
-Timing: HIP events on the stream the kernels run on (torch's current stream),
-bracketing the K timed steps and every launch inside them, after W warm-up steps.
-``roofline`` is for the dominant kernel (the N = 13824 GEMV).
+Timing: after W eager warm-up steps, the K timed steps are captured into one
+HIP graph and replayed between two HIP events on the stream the kernels run on
+(torch's current stream), so host-side launch cost is excluded. ``roofline`` is
+for the dominant kernel (the N = 13824 GEMV), timed the same way on its own.
 
 Also reported: ``cpu_baseline``, the CPU oracle timed on the host cores on a
 bounded sample of the same workload, and ``suite``, every other workload of the
@@ -126,24 +127,32 @@ class Case:
 
 
 def time_steps(torch, cases, steps, warmup):
-    """Run `steps` steps (each launches every case once) after `warmup` steps.
-    Returns (total seconds, per-case list of per-launch seconds)."""
+    """Time `steps` steps (each launches every case once, in order) after `warmup`
+    eager steps. The timed launches are captured into one HIP graph and replayed
+    between two events on the stream they run on, so the host's per-launch cost
+    (Python argument marshalling) is not part of the measurement. Returns seconds."""
     for _ in range(warmup):
         for c in cases:
             c.launch()
     torch.cuda.synchronize()
-    n = len(cases)
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps * n + 1)]
-    ev[0].record()
-    for s in range(steps):
-        for j, c in enumerate(cases):
-            c.launch()
-            ev[s * n + j + 1].record()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        for _ in range(steps):
+            for c in cases:
+                c.launch()
     torch.cuda.synchronize()
-    total = ev[0].elapsed_time(ev[-1]) / 1e3
-    per = [[ev[s * n + j].elapsed_time(ev[s * n + j + 1]) / 1e3 for s in range(steps)]
-           for j in range(n)]
-    return total, per
+    graph.replay()                      # first replay uploads the graph
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    del graph
+    return e0.elapsed_time(e1) / 1e3
 
 
 def cpu_baseline(problems, budget_s=10.0):
@@ -167,19 +176,14 @@ def cpu_baseline(problems, budget_s=10.0):
                       f"N=13824, 4-bit, M=1) in {el:.1f} s, f64, {threads} threads"}
 
 
-def summarize(case, secs, name):
-    a = np.array(secs)
-    med = float(np.median(a))
-    mean = float(a.mean())
-    d = {"workload": name, "us_median": round(med * 1e6, 3), "us_mean": round(mean * 1e6, 3),
-         "us_p10": round(float(np.percentile(a, 10)) * 1e6, 3),
-         "us_p90": round(float(np.percentile(a, 90)) * 1e6, 3),
-         "GB_s": round(case.bytes / mean / 1e9, 1),
-         "hbm_frac": round(case.bytes / mean / 1e9 / HBM_PEAK_GBS, 4),
-         "TFLOP_s": round(case.flops / mean / 1e12, 2),
-         "mfma_frac": round(case.flops / mean / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
-         "bytes": case.bytes, "flops": case.flops, "copies": case.copies}
-    return d
+def summarize(case, secs_per_launch, name):
+    t = secs_per_launch
+    return {"workload": name, "us_per_launch": round(t * 1e6, 3),
+            "GB_s": round(case.bytes / t / 1e9, 1),
+            "hbm_frac": round(case.bytes / t / 1e9 / HBM_PEAK_GBS, 4),
+            "TFLOP_s": round(case.flops / t / 1e12, 2),
+            "mfma_frac": round(case.flops / t / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+            "bytes": case.bytes, "flops": case.flops, "copies": case.copies}
 
 
 def main():
@@ -213,20 +217,22 @@ def main():
     log(f"inputs generated in {time.perf_counter() - t0:.1f} s")
     ca = Case(torch, pa, "qmv", torch.bfloat16)
     cb = Case(torch, pb, "qmv", torch.bfloat16)
-    total, per = time_steps(torch, [ca, cb], args.steps, args.warmup)
+    total = time_steps(torch, [ca, cb], args.steps, args.warmup)
     step_bytes = ca.bytes + cb.bytes
     value = step_bytes * args.steps / total / 1e9
     log(f"headline: {args.steps} steps in {total * 1e3:.3f} ms -> {value:.1f} GB/s")
+    # Each kernel alone, same launch configuration, for the per-kernel roofline.
+    ta = time_steps(torch, [ca], args.steps, args.warmup) / args.steps
+    tb = time_steps(torch, [cb], args.steps, args.warmup) / args.steps
 
     src_hash = kernel_sources_hash()
-    dom_mean = float(np.mean(per[1]))
-    achieved = cb.bytes / dom_mean / 1e9
+    achieved = cb.bytes / tb / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": read_traffic("qmv_K5120_N13824_b4_traffic", src_hash),
-                "kernel": "qmv_kernel<4,1,4,3> (K=5120, N=13824, 4-bit)",
+                "kernel": "qmv_mfma_kernel<4,1,4> (K=5120, N=13824, 4-bit, M=1)",
                 "algorithmic_bytes_per_launch": cb.bytes,
-                "avg_launch_us": round(dom_mean * 1e6, 3)}
+                "avg_launch_us": round(tb * 1e6, 3)}
 
     result = {
         "metric": "qmv HBM GB/s (% of peak); qmm & MoE gather_qmm TFLOPS (% of MFMA peak)",
@@ -248,7 +254,7 @@ def main():
                    "rotating_copies": ca.copies,
                    "kernel_sources_sha256_16": src_hash},
         "roofline": roofline,
-        "per_kernel": [summarize(ca, per[0], pa.name), summarize(cb, per[1], pb.name)],
+        "per_kernel": [summarize(ca, ta, pa.name), summarize(cb, tb, pb.name)],
     }
     del ca, cb
     torch.cuda.empty_cache()
@@ -264,9 +270,9 @@ def main():
             p = make()
             c = Case(torch, p, kind, torch.bfloat16)
             steps = max(20, args.steps // 2)
-            _, per1 = time_steps(torch, [c], steps, max(5, args.warmup // 2))
-            s = summarize(c, per1[0], p.name)
-            log(f"suite {p.name}: {s['us_mean']} us, {s['GB_s']} GB/s, {s['TFLOP_s']} TFLOP/s")
+            t1 = time_steps(torch, [c], steps, max(5, args.warmup // 2)) / steps
+            s = summarize(c, t1, p.name)
+            log(f"suite {p.name}: {s['us_per_launch']} us, {s['GB_s']} GB/s, {s['TFLOP_s']} TFLOP/s")
             suite.append(s)
             del c
             torch.cuda.empty_cache()

@@ -50,10 +50,30 @@ __device__ __forceinline__ uint32_t perm_b32(uint32_t hi, uint32_t lo, uint32_t 
   return __builtin_amdgcn_perm(hi, lo, sel);
 }
 
-// Wave-wide sum (all 64 lanes receive it).
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+// v_and_or_b32 (a & m) | c. Written out because gfx9 VOP3 encodings take no
+// literal operands: given two constants the compiler splits it into v_and + v_or.
+// The mask lives in an SGPR, the OR constant in a VGPR.
+__device__ __forceinline__ uint32_t and_or_b32(uint32_t a, uint32_t m, uint32_t c) {
+  uint32_t d;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "s"(m), "v"(c));
+  return d;
+}
+
+// Wave-wide sum with DPP lane moves (VALU only, no LDS round trips). Rows of 16
+// lanes are summed with quad permutes and mirrors; row_bcast then carries row
+// sums upward. The full sum ends in lane 63 (other lanes hold partial sums).
+template <int CTRL, int ROW_MASK, bool BOUND_CTRL>
+__device__ __forceinline__ float dpp_add(float v) {
+  return v + __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL,
+                                                                ROW_MASK, 0xF, BOUND_CTRL));
+}
+__device__ __forceinline__ float wave_sum_lane63(float v) {
+  v = dpp_add<0xB1, 0xF, true>(v);    // quad_perm [1,0,3,2]
+  v = dpp_add<0x4E, 0xF, true>(v);    // quad_perm [2,3,0,1]
+  v = dpp_add<0x141, 0xF, true>(v);   // row_half_mirror
+  v = dpp_add<0x140, 0xF, true>(v);   // row_mirror: every lane holds its row's sum
+  v = dpp_add<0x142, 0xA, false>(v);  // row_bcast:15 into rows 1 and 3
+  v = dpp_add<0x143, 0xC, false>(v);  // row_bcast:31 into rows 2 and 3
   return v;
 }
 

@@ -20,6 +20,8 @@
 // matrix-core path is the MI355X replacement for both.
 #pragma once
 
+#include <type_traits>
+
 #include "common.hpp"
 
 namespace bitmm {
@@ -82,6 +84,12 @@ struct MmTile {
   // One output tile. x_rows: first activation row of the tile (row stride K);
   // rows: valid rows (<= BM); w, s, b: the weight slab ([N, K*BITS/32], [N, K/64]);
   // y_rows: first output row (row stride N).
+  //
+  // Pipeline: weight chunks are requested two K steps ahead (their HBM latency is
+  // longer than one step of MFMAs); the x tile one step ahead, into the other LDS
+  // buffer. Loads are branch-free (out-of-range rows and k re-read valid memory and
+  // are zeroed by a select) and scales/biases stay raw bf16 until use, so nothing
+  // forces a wait on the loads before the step's MFMAs are issued.
   __device__ static void run(const uint16_t* __restrict__ x_rows, int rows,
                              const uint32_t* __restrict__ w, const uint16_t* __restrict__ sc,
                              const uint16_t* __restrict__ bi, int n0, int N, int K,
@@ -113,77 +121,83 @@ struct MmTile {
 #pragma unroll
       for (int nb = 0; nb < NBW; ++nb) acc[mb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    // x tile pieces owned by this thread.
+    // x tile pieces owned by this thread (row r, 16-byte column c of the step).
     u32x4_t xs[XPER];
     auto load_x = [&](int step) {
 #pragma unroll
       for (int i = 0; i < XPER; ++i) {
-        const int id = i * THREADS + tid;
-        const int r = id / PIECES_PER_ROW;
-        const int c = id % PIECES_PER_ROW;
-        u32x4_t v = {0u, 0u, 0u, 0u};
-        const int k = step * KSTEP + c * 8;
-        if (id < XPIECES && r < rows && k < K) v = load_u128(x_rows + (int64_t)r * K + k);
-        xs[i] = v;
+        const int id = min(i * THREADS + tid, XPIECES - 1);
+        const int r = min(id / PIECES_PER_ROW, rows - 1);
+        const int k = min(step * KSTEP + (id % PIECES_PER_ROW) * 8, K - 8);
+        xs[i] = load_u128(x_rows + (int64_t)r * K + k);
       }
     };
-    auto store_x = [&](int buf) {
+    auto store_x = [&](int buf, int step) {
 #pragma unroll
       for (int i = 0; i < XPER; ++i) {
         const int id = i * THREADS + tid;
         if (id < XPIECES) {
           const int r = id / PIECES_PER_ROW;
           const int c = id % PIECES_PER_ROW;
-          *reinterpret_cast<u32x4_t*>(lds + buf * BUF + r * PITCH + c * 16) = xs[i];
+          const bool ok = r < rows && step * KSTEP + c * 8 < K;
+          *reinterpret_cast<u32x4_t*>(lds + buf * BUF + r * PITCH + c * 16) =
+              ok ? xs[i] : u32x4_t{0u, 0u, 0u, 0u};
         }
       }
     };
 
-    u32x4_t qc[NBW];
-    float sv[NBW], bv[NBW];
-    auto load_w = [&](int step) {
-      const int k = step * KSTEP + lj * CC;
-      const bool kok = k < K;  // chunks past K (half step) dequantize to zero
-      const int g = kok ? k / kGroup : 0;
+    // Weight prefetch ring, two steps deep (slot = step & 1).
+    u32x4_t qc[2][NBW];
+    uint16_t sr[2][NBW], br[2][NBW];
+    auto load_w = [&](int step, u32x4_t (&q)[NBW], uint16_t (&s)[NBW], uint16_t (&b)[NBW]) {
+      const int k = min(step * KSTEP + lj * CC, K - CC);  // past K: re-read, zeroed below
+      const int g = k / kGroup;
+      const int64_t off = (int64_t)k * BITS / 32 - lj * 4;
 #pragma unroll
       for (int nb = 0; nb < NBW; ++nb) {
-        qc[nb] = kok ? load_stream(wp[nb] + (int64_t)step * (KSTEP * BITS / 32))
-                     : u32x4_t{0u, 0u, 0u, 0u};
-        sv[nb] = kok ? bf16_to_f32(sp[nb][g]) : 0.f;
-        bv[nb] = kok ? bf16_to_f32(bp[nb][g]) : 0.f;
+        q[nb] = load_stream(wp[nb] + off);
+        s[nb] = sp[nb][g];
+        b[nb] = bp[nb][g];
       }
     };
 
-    load_x(0);
-    load_w(0);
-    store_x(0);
-    __syncthreads();
-
-    for (int step = 0; step < nsteps; ++step) {
+    auto body = [&](int step, auto slot_c) {
+      constexpr int slot = decltype(slot_c)::value;
       const int buf = step & 1;
-      // Dequantize this step's weights, then prefetch the next step.
+      const bool kok = step * KSTEP + lj * CC < K;  // chunks past K dequantize to zero
       bf16x8_t bop[NBW][SUB];
 #pragma unroll
-      for (int nb = 0; nb < NBW; ++nb) dequant(qc[nb], sv[nb], bv[nb], bop[nb]);
+      for (int nb = 0; nb < NBW; ++nb)
+        dequant(qc[slot][nb], kok ? bf16_to_f32(sr[slot][nb]) : 0.f,
+                kok ? bf16_to_f32(br[slot][nb]) : 0.f, bop[nb]);
+      if (step + 2 < nsteps) load_w(step + 2, qc[slot], sr[slot], br[slot]);
       const bool more = step + 1 < nsteps;
-      if (more) {
-        load_x(step + 1);
-        load_w(step + 1);
-      }
+      if (more) load_x(step + 1);
       const char* ab = lds + buf * BUF + ln * PITCH + lj * CC * 2;
 #pragma unroll
       for (int t = 0; t < SUB; ++t) {
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
-          const bf16x8_t a =
-              __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(ab + mb * 16 * PITCH + t * 16));
+          const bf16x8_t a = __builtin_bit_cast(
+              bf16x8_t, *reinterpret_cast<const u32x4_t*>(ab + mb * 16 * PITCH + t * 16));
 #pragma unroll
           for (int nb = 0; nb < NBW; ++nb)
             acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bop[nb][t], acc[mb][nb], 0, 0, 0);
         }
       }
-      if (more) store_x(buf ^ 1);
+      if (more) store_x(buf ^ 1, step + 1);
       __syncthreads();
+    };
+
+    load_w(0, qc[0], sr[0], br[0]);
+    if (nsteps > 1) load_w(1, qc[1], sr[1], br[1]);
+    load_x(0);
+    store_x(0, 0);
+    __syncthreads();
+
+    for (int step = 0; step < nsteps; step += 2) {
+      body(step, std::integral_constant<int, 0>{});
+      if (step + 1 < nsteps) body(step + 1, std::integral_constant<int, 1>{});
     }
 
     // Epilogue: lane holds rows 4*lj + i of column ln in each 16x16 block.

@@ -67,81 +67,83 @@ __global__ __launch_bounds__(kQmvThreads) void qmv_kernel(QmvParams p) {
     for (int m = 0; m < MR; ++m) acc[r][m] = 0.f;
 
   for (int kb = 0; kb < nch; kb += kWave * CPL) {
-    // 1. Weight stream: every chunk of every row, up front.
+    // 1. Every load of this pass, with no arithmetic between them: codes of all
+    //    RPW rows, their scales and biases (kept as raw bits), then activations.
+    //    Chunks past the end of the row re-read the last chunk (in bounds) and are
+    //    zeroed through their activations below.
     u32x4_t q[CPL][RPW];
-    float sv[CPL][RPW], bv[CPL][RPW];
+    uint16_t sraw[CPL][RPW], braw[CPL][RPW];
+    u32x4_t xr[CPL][MR][XU];
     bool ok[CPL];
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
       const int c = kb + i * kWave + lane;
       ok[i] = c < nch;
-      const int cc = ok[i] ? c : 0;
+      const int cc = ok[i] ? c : nch - 1;
       const int g = cc * CC / kGroup;
 #pragma unroll
       for (int r = 0; r < RPW; ++r) {
         q[i][r] = load_stream(wr[r] + 4 * (int64_t)cc);
-        sv[i][r] = bf16_to_f32(sr[r][g]);
-        bv[i][r] = bf16_to_f32(br[r][g]);
+        sraw[i][r] = sr[r][g];
+        braw[i][r] = br[r][g];
       }
-    }
-    // 2. Activations for the same chunks (L1/L2 resident, shared by all waves).
-    u32x4_t xr[CPL][MR][XU];
-#pragma unroll
-    for (int i = 0; i < CPL; ++i) {
-      const int cc = ok[i] ? kb + i * kWave + lane : 0;
 #pragma unroll
       for (int m = 0; m < MR; ++m) {
         const uint16_t* xp = p.x + (int64_t)m * p.K + (int64_t)cc * CC;
 #pragma unroll
-        for (int u = 0; u < XU; ++u) {
-          const u32x4_t v = load_u128(xp + 8 * u);
-          xr[i][m][u] = ok[i] ? v : u32x4_t{0u, 0u, 0u, 0u};
-        }
+        for (int u = 0; u < XU; ++u) xr[i][m][u] = load_u128(xp + 8 * u);
       }
     }
-    // 3. Arithmetic.
+    // Keep the compiler from pulling arithmetic (and the waits it implies) in
+    // between the loads above.
+    __builtin_amdgcn_sched_barrier(0);
+
+    // 2. Arithmetic.
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
+#pragma unroll
+      for (int m = 0; m < MR; ++m)
+#pragma unroll
+        for (int u = 0; u < XU; ++u)
+          if (!ok[i]) xr[i][m][u] = u32x4_t{0u, 0u, 0u, 0u};
       if constexpr (BITS == 4) {
-        // Activation pairs matching the nibble pairs (i, i+4) of each word.
+        // Activation pairs matching the nibble pairs (j, j+4) of each word.
         uint32_t xp[MR][4][4];
         float sx[MR];
 #pragma unroll
         for (int m = 0; m < MR; ++m) {
-          const uint32_t* xd = reinterpret_cast<const uint32_t*>(&xr[i][m][0]);
           float t = 0.f;
 #pragma unroll
           for (int wd = 0; wd < 4; ++wd) {
-            const uint32_t d0 = xd[4 * wd + 0], d1 = xd[4 * wd + 1];
-            const uint32_t d2 = xd[4 * wd + 2], d3 = xd[4 * wd + 3];
-            xp[m][wd][0] = perm_b32(d2, d0, 0x05040100u);  // (x0, x4)
-            xp[m][wd][1] = perm_b32(d2, d0, 0x07060302u);  // (x1, x5)
-            xp[m][wd][2] = perm_b32(d3, d1, 0x05040100u);  // (x2, x6)
-            xp[m][wd][3] = perm_b32(d3, d1, 0x07060302u);  // (x3, x7)
-            t = dot2_bf16(d0, 0x3F803F80u, t);
-            t = dot2_bf16(d1, 0x3F803F80u, t);
-            t = dot2_bf16(d2, 0x3F803F80u, t);
-            t = dot2_bf16(d3, 0x3F803F80u, t);
+            const u32x4_t d = xr[i][m][wd];
+            xp[m][wd][0] = perm_b32(d[2], d[0], 0x05040100u);  // (x0, x4)
+            xp[m][wd][1] = perm_b32(d[2], d[0], 0x07060302u);  // (x1, x5)
+            xp[m][wd][2] = perm_b32(d[3], d[1], 0x05040100u);  // (x2, x6)
+            xp[m][wd][3] = perm_b32(d[3], d[1], 0x07060302u);  // (x3, x7)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) t = dot2_bf16(d[e], 0x3F803F80u, t);
           }
           sx[m] = t;
         }
+        const uint32_t magic = 0x43004300u;  // bf16 pair (128, 128)
 #pragma unroll
         for (int r = 0; r < RPW; ++r) {
-          const uint32_t wq[4] = {q[i][r][0], q[i][r][1], q[i][r][2], q[i][r][3]};
           float P[MR];
 #pragma unroll
           for (int m = 0; m < MR; ++m) P[m] = 0.f;
 #pragma unroll
           for (int wd = 0; wd < 4; ++wd) {
+            const uint32_t w0 = q[i][r][wd];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-              const uint32_t qp = ((wq[wd] >> (4 * j)) & 0x000F000Fu) | 0x43004300u;
+              // bf16 pair (128 + q_j, 128 + q_{j+4}), exact.
+              const uint32_t qp = and_or_b32(w0 >> (4 * j), 0x000F000Fu, magic);
 #pragma unroll
               for (int m = 0; m < MR; ++m) P[m] = dot2_bf16(qp, xp[m][wd][j], P[m]);
             }
           }
-          const float s = sv[i][r];
-          const float cb = fmaf(-128.f, s, bv[i][r]);
+          const float s = bf16_to_f32(sraw[i][r]);
+          const float cb = fmaf(-128.f, s, bf16_to_f32(braw[i][r]));
 #pragma unroll
           for (int m = 0; m < MR; ++m) acc[r][m] = fmaf(s, P[m], fmaf(cb, sx[m], acc[r][m]));
         }
@@ -150,34 +152,36 @@ __global__ __launch_bounds__(kQmvThreads) void qmv_kernel(QmvParams p) {
         float sx[MR];
 #pragma unroll
         for (int m = 0; m < MR; ++m) {
-          const uint32_t* xd = reinterpret_cast<const uint32_t*>(&xr[i][m][0]);
           float t = 0.f;
 #pragma unroll
-          for (int d = 0; d < 8; ++d) {
-            xf[m][2 * d] = bf16_lo(xd[d]);
-            xf[m][2 * d + 1] = bf16_hi(xd[d]);
-            t += xf[m][2 * d];
-            t += xf[m][2 * d + 1];
+          for (int u = 0; u < 2; ++u) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const uint32_t d = xr[i][m][u][e];
+              xf[m][8 * u + 2 * e] = bf16_lo(d);
+              xf[m][8 * u + 2 * e + 1] = bf16_hi(d);
+              t = dot2_bf16(d, 0x3F803F80u, t);
+            }
           }
           sx[m] = t;
         }
 #pragma unroll
         for (int r = 0; r < RPW; ++r) {
-          const uint32_t wq[4] = {q[i][r][0], q[i][r][1], q[i][r][2], q[i][r][3]};
           float P[MR];
 #pragma unroll
           for (int m = 0; m < MR; ++m) P[m] = 0.f;
 #pragma unroll
           for (int wd = 0; wd < 4; ++wd) {
+            const uint32_t w0 = q[i][r][wd];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-              const float qf = (float)((wq[wd] >> (8 * j)) & 0xFFu);
+              const float qf = (float)((w0 >> (8 * j)) & 0xFFu);  // v_cvt_f32_ubyte<j>
 #pragma unroll
               for (int m = 0; m < MR; ++m) P[m] = fmaf(xf[m][4 * wd + j], qf, P[m]);
             }
           }
-          const float s = sv[i][r];
-          const float b = bv[i][r];
+          const float s = bf16_to_f32(sraw[i][r]);
+          const float b = bf16_to_f32(braw[i][r]);
 #pragma unroll
           for (int m = 0; m < MR; ++m) acc[r][m] = fmaf(s, P[m], fmaf(b, sx[m], acc[r][m]));
         }
@@ -185,14 +189,14 @@ __global__ __launch_bounds__(kQmvThreads) void qmv_kernel(QmvParams p) {
     }
   }
 
-  // 4. Wave reductions; lane 0 stores.
+  // 3. Wave reductions; lane 63 holds each sum and stores it.
 #pragma unroll
   for (int r = 0; r < RPW; ++r) {
 #pragma unroll
     for (int m = 0; m < MR; ++m) {
-      const float v = wave_sum(acc[r][m]);
+      const float v = wave_sum_lane63(acc[r][m]);
       const int n = n0 + r;
-      if (lane == 0 && n < p.N) {
+      if (lane == kWave - 1 && n < p.N) {
         const int64_t o = (int64_t)m * p.N + n;
         if (p.out_f32)
           static_cast<float*>(p.y)[o] = v;
@@ -200,6 +204,152 @@ __global__ __launch_bounds__(kQmvThreads) void qmv_kernel(QmvParams p) {
           static_cast<uint16_t*>(p.y)[o] = f32_to_bf16(v);
       }
     }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Decode GEMV (M = 1), streaming form. Lane l owns the 16-byte chunks
+// l, l+64, ... (at most CPL of them) of EVERY row, so its activation chunks are
+// loaded, rearranged and summed once per wave and stay in registers. The wave
+// then walks a block of `rpw` consecutive rows with a ring of three row buffers:
+// the loads of row n+2 are issued before row n is computed, so two rows of
+// codes are in flight behind the arithmetic. Each row ends with a DPP reduction.
+// ---------------------------------------------------------------------------
+template <int BITS, int CPL>
+__global__ __launch_bounds__(kQmvThreads) void qmv_stream_kernel(QmvParams p, int rpw) {
+  constexpr int CC = 128 / BITS;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = blockIdx.x * kQmvWaves + (threadIdx.x >> 6);
+  const int nfirst = wave * rpw;
+  if (nfirst >= p.N) return;  // uniform per wave
+  const int nend = min(nfirst + rpw, p.N);
+  const int nch = p.K / CC;
+  const int G = p.K / kGroup;
+  const int64_t wrow = (int64_t)p.K * BITS / 32;
+
+  int cidx[CPL], gidx[CPL];
+  bool ok[CPL];
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) {
+    const int c = i * kWave + lane;
+    ok[i] = c < nch;
+    cidx[i] = ok[i] ? c : nch - 1;
+    gidx[i] = cidx[i] * CC / kGroup;
+  }
+
+  // Activations, once per wave.
+  constexpr int XD = CC / 2;  // activation dwords (bf16 pairs) per chunk
+  uint32_t xraw[CPL][XD];
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) {
+#pragma unroll
+    for (int u = 0; u < XD / 4; ++u) {
+      const u32x4_t v = load_u128(p.x + (int64_t)cidx[i] * CC + 8 * u);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) xraw[i][4 * u + e] = ok[i] ? v[e] : 0u;
+    }
+  }
+  float sx[CPL];
+  // 4-bit: activation pairs (x_j, x_{j+4}) of each word; 8-bit: f32 activations.
+  uint32_t xp[BITS == 4 ? CPL : 1][4][4];
+  float xf[BITS == 8 ? CPL : 1][16];
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) {
+    float t = 0.f;
+#pragma unroll
+    for (int d = 0; d < XD; ++d) t = dot2_bf16(xraw[i][d], 0x3F803F80u, t);
+    sx[i] = t;
+    if constexpr (BITS == 4) {
+#pragma unroll
+      for (int wd = 0; wd < 4; ++wd) {
+        const uint32_t d0 = xraw[i][4 * wd], d1 = xraw[i][4 * wd + 1];
+        const uint32_t d2 = xraw[i][4 * wd + 2], d3 = xraw[i][4 * wd + 3];
+        xp[i][wd][0] = perm_b32(d2, d0, 0x05040100u);  // (x0, x4)
+        xp[i][wd][1] = perm_b32(d2, d0, 0x07060302u);  // (x1, x5)
+        xp[i][wd][2] = perm_b32(d3, d1, 0x05040100u);  // (x2, x6)
+        xp[i][wd][3] = perm_b32(d3, d1, 0x07060302u);  // (x3, x7)
+      }
+    } else {
+#pragma unroll
+      for (int d = 0; d < 8; ++d) {
+        xf[i][2 * d] = bf16_lo(xraw[i][d]);
+        xf[i][2 * d + 1] = bf16_hi(xraw[i][d]);
+      }
+    }
+  }
+
+  struct Row {
+    u32x4_t q[CPL];
+    uint16_t s[CPL], b[CPL];
+  };
+  auto load_row = [&](int n, Row& R) {
+    const uint32_t* wr = p.w + (int64_t)n * wrow;
+    const uint16_t* sr = p.s + (int64_t)n * G;
+    const uint16_t* br = p.b + (int64_t)n * G;
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+      R.q[i] = load_stream(wr + 4 * (int64_t)cidx[i]);
+      R.s[i] = sr[gidx[i]];
+      R.b[i] = br[gidx[i]];
+    }
+  };
+  const uint32_t magic = 0x43004300u;  // bf16 pair (128, 128)
+  auto compute_row = [&](int n, const Row& R) {
+    float acc = 0.f;
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+      const float s = bf16_to_f32(R.s[i]);
+      const float b = bf16_to_f32(R.b[i]);
+      if constexpr (BITS == 4) {
+        float P[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int wd = 0; wd < 4; ++wd) {
+          const uint32_t w0 = R.q[i][wd];
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            P[j] = dot2_bf16(and_or_b32(w0 >> (4 * j), 0x000F000Fu, magic), xp[i][wd][j], P[j]);
+        }
+        const float Pt = (P[0] + P[1]) + (P[2] + P[3]);
+        acc = fmaf(s, Pt, fmaf(fmaf(-128.f, s, b), sx[i], acc));
+      } else {
+        float P[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int wd = 0; wd < 4; ++wd) {
+          const uint32_t w0 = R.q[i][wd];
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            P[j] = fmaf(xf[i][4 * wd + j], (float)((w0 >> (8 * j)) & 0xFFu), P[j]);
+        }
+        const float Pt = (P[0] + P[1]) + (P[2] + P[3]);
+        acc = fmaf(s, Pt, fmaf(b, sx[i], acc));
+      }
+    }
+    const float v = wave_sum_lane63(acc);
+    if (lane == kWave - 1 && n < nend) {
+      if (p.out_f32)
+        static_cast<float*>(p.y)[n] = v;
+      else
+        static_cast<uint16_t*>(p.y)[n] = f32_to_bf16(v);
+    }
+  };
+
+  // Every load is unconditional: past the wave's last row the row index clamps to
+  // that row (an L2 hit, never another wave's row), so the compiler can count
+  // outstanding loads exactly and wait only for the row it is about to use.
+  const int nlast = nend - 1;
+  Row ring[3];
+  load_row(nfirst, ring[0]);
+  load_row(min(nfirst + 1, nlast), ring[1]);
+  for (int n = nfirst; n < nend; n += 3) {
+    load_row(min(n + 2, nlast), ring[2]);
+    __builtin_amdgcn_sched_barrier(0);
+    compute_row(n, ring[0]);
+    load_row(min(n + 3, nlast), ring[0]);
+    __builtin_amdgcn_sched_barrier(0);
+    compute_row(n + 1, ring[1]);
+    load_row(min(n + 4, nlast), ring[1]);
+    __builtin_amdgcn_sched_barrier(0);
+    compute_row(n + 2, ring[2]);
   }
 }
 
@@ -230,6 +380,29 @@ hipError_t pick_cpl(const QmvParams& p, int cpl, hipStream_t stream) {
   }
 }
 
+template <int BITS, int CPL>
+hipError_t launch_stream(const QmvParams& p, int rpw, hipStream_t stream) {
+  const int waves = (p.N + rpw - 1) / rpw;
+  const int blocks = (waves + kQmvWaves - 1) / kQmvWaves;
+  hipLaunchKernelGGL((qmv_stream_kernel<BITS, CPL>), dim3(blocks), dim3(kQmvThreads), 0, stream, p,
+                     rpw);
+  return hipGetLastError();
+}
+
+// Streaming form: M = 1 with every chunk of a row covered in one pass
+// (chunks per lane <= 5). Returns hipErrorNotSupported otherwise.
+template <int BITS>
+hipError_t launch_stream_bits(const QmvParams& p, int cpl, int rpw, hipStream_t stream) {
+  switch (cpl) {
+    case 1: return launch_stream<BITS, 1>(p, rpw, stream);
+    case 2: return launch_stream<BITS, 2>(p, rpw, stream);
+    case 3: return launch_stream<BITS, 3>(p, rpw, stream);
+    case 4: return launch_stream<BITS, 4>(p, rpw, stream);
+    case 5: return launch_stream<BITS, 5>(p, rpw, stream);
+    default: return hipErrorNotSupported;
+  }
+}
+
 template <int BITS>
 hipError_t launch_bits(const QmvParams& p, int mr, int cpl, hipStream_t stream) {
   switch (mr) {
@@ -249,5 +422,7 @@ hipError_t launch_bits(const QmvParams& p, int mr, int cpl, hipStream_t stream) 
 // One explicit instantiation per bit width, each in its own translation unit.
 extern template hipError_t qmv_detail::launch_bits<4>(const qmv_detail::QmvParams&, int, int, hipStream_t);
 extern template hipError_t qmv_detail::launch_bits<8>(const qmv_detail::QmvParams&, int, int, hipStream_t);
+extern template hipError_t qmv_detail::launch_stream_bits<4>(const qmv_detail::QmvParams&, int, int, hipStream_t);
+extern template hipError_t qmv_detail::launch_stream_bits<8>(const qmv_detail::QmvParams&, int, int, hipStream_t);
 
 }  // namespace bitmm

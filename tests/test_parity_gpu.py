@@ -51,6 +51,19 @@ def test_qmv_small(M, N, K, bits, out):
     G.assert_close(got, oracle_dense(d), out, f"qmv M{M} N{N} K{K} b{bits}")
 
 
+@pytest.mark.parametrize("path", ["stream", "valu", "mfma"])
+@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("M,N,K", [(1, 300, 640), (1, 64, 8256), (1, 33, 192), (3, 130, 5120),
+                                   (8, 40, 576)])
+def test_qmv_every_kernel(M, N, K, bits, path, monkeypatch):
+    """Each GEMV kernel form (chosen with the BITMM_QMV_PATH knob) against the oracle,
+    f32 output, where the exact-product rule applies."""
+    monkeypatch.setenv("BITMM_QMV_PATH", path)
+    d = I.random_dense(M, N, K, bits, seed=11 * M + N + K)
+    got = G.to_f64(G.run_dense("bitmm_qmv", d, "f32"))
+    G.assert_close(got, oracle_dense(d), "f32", f"qmv[{path}] M{M} N{N} K{K} b{bits}")
+
+
 @pytest.mark.parametrize("bits", [4, 8])
 @pytest.mark.parametrize("out", ["bf16", "f32"])
 @pytest.mark.parametrize("M,N,K", [(1, 130, 320), (2, 64, 128), (3, 200, 640), (5, 33, 192),
