@@ -12,8 +12,11 @@
 //      row range from the workspace and runs the shared matrix-core tile over those
 //      rows, so each expert's codes are streamed once per column block however many
 //      rows the expert has. Experts without rows exit at once.
+#include <stdlib.h>
+
 #include "kernels.hpp"
 #include "mfma_tile.hpp"
+#include "mfma_tile2.hpp"
 
 namespace bitmm {
 namespace {
@@ -73,9 +76,8 @@ __device__ __forceinline__ int xcd_remap(int b, int total) {
   return (b % 8) * (total / 8) + b / 8;
 }
 
-template <int BITS, int MB, int NBW, int WAVES>
-__global__ __launch_bounds__(64 * WAVES) void gather_qmm_kernel(GatherParams p) {
-  using T = MmTile<BITS, MB, NBW, WAVES>;
+template <int BITS, typename T>
+__global__ __launch_bounds__(T::THREADS) void gather_qmm_kernel(GatherParams p) {
   __shared__ __attribute__((aligned(16))) char lds[T::LDS_BYTES];
   // Consecutive logical ids (all column blocks of one expert) share an XCD, so the
   // expert's activation rows are fetched into one L2.
@@ -119,13 +121,17 @@ __global__ __launch_bounds__(64 * WAVES) void gather_qmm_kernel(GatherParams p) 
   }
 }
 
-template <int BITS, int MB, int NBW, int WAVES>
+template <int BITS, typename T>
 hipError_t launch_grouped(GatherParams p, hipStream_t stream) {
-  using T = MmTile<BITS, MB, NBW, WAVES>;
   p.tiles_n = (p.N + T::BN - 1) / T::BN;
-  hipLaunchKernelGGL((gather_qmm_kernel<BITS, MB, NBW, WAVES>), dim3(p.E * p.tiles_n),
-                     dim3(T::THREADS), 0, stream, p);
+  hipLaunchKernelGGL((gather_qmm_kernel<BITS, T>), dim3(p.E * p.tiles_n), dim3(T::THREADS), 0,
+                     stream, p);
   return hipGetLastError();
+}
+
+int tile_form() {
+  const char* e = getenv("BITMM_MM_TILE");
+  return (e && e[0] == '1') ? 1 : 2;
 }
 
 }  // namespace
@@ -157,8 +163,12 @@ hipError_t launch_gather_qmm(const uint16_t* x, const uint32_t* w, const uint16_
   p.E = (int)E;
   p.tiles_n = 0;
   p.out_f32 = out_f32 ? 1 : 0;
-  if (bits == 4) return launch_grouped<4, 4, 2, 4>(p, stream);
-  return launch_grouped<8, 4, 2, 4>(p, stream);
+  if (tile_form() == 1) {
+    if (bits == 4) return launch_grouped<4, MmTile<4, 4, 2, 4>>(p, stream);
+    return launch_grouped<8, MmTile<8, 4, 2, 4>>(p, stream);
+  }
+  if (bits == 4) return launch_grouped<4, MmTile2<4, 4, 2, 4>>(p, stream);
+  return launch_grouped<8, MmTile2<8, 4, 2, 4>>(p, stream);
 }
 
 }  // namespace bitmm

@@ -1,8 +1,11 @@
 // Dense prefill GEMM on the matrix cores (M >= 8): y[M, N] = x[M, K] * dequant(w)^T.
 // The epic's kernel table puts the prefill quantized GEMM at 82% of GPU time; the
 // tile itself lives in mfma_tile.hpp.
+#include <stdlib.h>
+
 #include "kernels.hpp"
 #include "mfma_tile.hpp"
+#include "mfma_tile2.hpp"
 
 namespace bitmm {
 namespace {
@@ -27,9 +30,8 @@ __device__ __forceinline__ int xcd_remap(int b, int total) {
   return (b % 8) * (total / 8) + b / 8;
 }
 
-template <int BITS, int MB, int NBW, int WAVES>
-__global__ __launch_bounds__(64 * WAVES) void qmm_mfma_kernel(QmmParams p) {
-  using T = MmTile<BITS, MB, NBW, WAVES>;
+template <typename T>
+__global__ __launch_bounds__(T::THREADS) void qmm_mfma_kernel(QmmParams p) {
   __shared__ __attribute__((aligned(16))) char lds[T::LDS_BYTES];
   const int total = p.tiles_m * p.tiles_n;
   const int L = xcd_remap(blockIdx.x, total);
@@ -42,14 +44,20 @@ __global__ __launch_bounds__(64 * WAVES) void qmm_mfma_kernel(QmmParams p) {
          static_cast<char*>(p.y) + (size_t)m0 * p.N * ysz, p.out_f32 != 0, lds);
 }
 
-template <int BITS, int MB, int NBW, int WAVES>
+template <typename T>
 hipError_t launch_tiles(QmmParams p, hipStream_t stream) {
-  using T = MmTile<BITS, MB, NBW, WAVES>;
   p.tiles_m = (p.M + T::BM - 1) / T::BM;
   p.tiles_n = (p.N + T::BN - 1) / T::BN;
-  hipLaunchKernelGGL((qmm_mfma_kernel<BITS, MB, NBW, WAVES>), dim3(p.tiles_m * p.tiles_n),
-                     dim3(T::THREADS), 0, stream, p);
+  hipLaunchKernelGGL((qmm_mfma_kernel<T>), dim3(p.tiles_m * p.tiles_n), dim3(T::THREADS), 0,
+                     stream, p);
   return hipGetLastError();
+}
+
+// Tile form: 2 = LDS-staged operands (default), 1 = weights straight to registers.
+// BITMM_MM_TILE selects one (comparison knob).
+int tile_form() {
+  const char* e = getenv("BITMM_MM_TILE");
+  return (e && e[0] == '1') ? 1 : 2;
 }
 
 }  // namespace
@@ -68,8 +76,12 @@ hipError_t launch_qmm_mfma(const uint16_t* x, const uint32_t* w, const uint16_t*
   p.K = (int)K;
   p.out_f32 = out_f32 ? 1 : 0;
   p.tiles_m = p.tiles_n = 0;
-  if (bits == 4) return launch_tiles<4, 8, 2, 4>(p, stream);
-  return launch_tiles<8, 8, 2, 4>(p, stream);
+  if (tile_form() == 1) {
+    if (bits == 4) return launch_tiles<MmTile<4, 8, 2, 4>>(p, stream);
+    return launch_tiles<MmTile<8, 8, 2, 4>>(p, stream);
+  }
+  if (bits == 4) return launch_tiles<MmTile2<4, 8, 2, 4>>(p, stream);
+  return launch_tiles<MmTile2<8, 8, 2, 4>>(p, stream);
 }
 
 }  // namespace bitmm
