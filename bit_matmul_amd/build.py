@@ -20,7 +20,7 @@ LIB = os.path.join(HERE, "libbitmm.so")
 ARCH = "gfx950"
 
 # Packed-FP32 VALU instructions are kept out of the device code.
-DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-mllvm", "-amdgpu-mfma-vgpr-form=1"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-fno-gpu-rdc",
           "-Wall", "-Wno-unused-function", "-I", os.path.join(ROOT, "include")]
 

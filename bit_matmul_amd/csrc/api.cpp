@@ -8,7 +8,7 @@
 
 #include <atomic>
 
-#include "../../include/bitmm.h"
+#include "bitmm.h"
 #include "kernels.hpp"
 
 namespace {

@@ -17,6 +17,7 @@
 #include "kernels.hpp"
 #include "mfma_tile.hpp"
 #include "mfma_tile2.hpp"
+#include "mfma_tile3.hpp"
 
 namespace bitmm {
 namespace {
@@ -131,7 +132,21 @@ hipError_t launch_grouped(GatherParams p, hipStream_t stream) {
 
 int tile_form() {
   const char* e = getenv("BITMM_MM_TILE");
-  return (e && e[0] == '1') ? 1 : 2;
+  if (e && (e[0] == '1' || e[0] == '2')) return e[0] - '0';
+  return 3;
+}
+
+// Pipelined tile, one row of 4 waves (each expert's weights dequantized once per
+// row block). Row blocks of 16 per tile from the mean rows per expert, with slack for
+// the spread of the routing: experts with more rows loop over row tiles.
+template <int BITS>
+hipError_t launch_tile3(GatherParams p, hipStream_t stream) {
+  const int64_t mean = p.E > 0 ? (p.B + p.E - 1) / p.E : p.B;
+  const int64_t blocks = (mean + mean / 4 + 15) / 16;
+  if (blocks <= 1) return launch_grouped<BITS, MmTile3<BITS, 1, 2, 1, 4>>(p, stream);
+  if (blocks <= 2) return launch_grouped<BITS, MmTile3<BITS, 2, 2, 1, 4>>(p, stream);
+  if (blocks <= 3) return launch_grouped<BITS, MmTile3<BITS, 3, 2, 1, 4>>(p, stream);
+  return launch_grouped<BITS, MmTile3<BITS, 4, 2, 1, 4>>(p, stream);
 }
 
 }  // namespace
@@ -167,8 +182,11 @@ hipError_t launch_gather_qmm(const uint16_t* x, const uint32_t* w, const uint16_
     if (bits == 4) return launch_grouped<4, MmTile<4, 4, 2, 4>>(p, stream);
     return launch_grouped<8, MmTile<8, 4, 2, 4>>(p, stream);
   }
-  if (bits == 4) return launch_grouped<4, MmTile2<4, 4, 2, 4>>(p, stream);
-  return launch_grouped<8, MmTile2<8, 4, 2, 4>>(p, stream);
+  if (tile_form() == 2) {
+    if (bits == 4) return launch_grouped<4, MmTile2<4, 4, 2, 4>>(p, stream);
+    return launch_grouped<8, MmTile2<8, 4, 2, 4>>(p, stream);
+  }
+  return bits == 4 ? launch_tile3<4>(p, stream) : launch_tile3<8>(p, stream);
 }
 
 }  // namespace bitmm

@@ -3,25 +3,28 @@
 // Why the staging: the MFMA operand layout wants 16 weight rows per instruction,
 // but a load instruction that reads 64 bytes from each of 16 rows streams from HBM
 // at a fraction of the rate of one reading whole 128-byte lines. So every operand
-// is fetched row-contiguously (8 rows x 128 bytes per wave instruction, 16 bytes
-// per lane) and written to LDS in a swizzled layout, where the MFMA lanes read it.
+// is fetched row-contiguously (16 bytes per lane, 8 rows x 128 bytes or 4 rows x
+// 256 bytes per wave instruction) and written to LDS in a swizzled layout, where
+// the MFMA lanes read it.
 //
 // Workgroup: WAVES waves; wave w owns RW = 16*NBW weight rows (columns of y) and
 // all BM = 16*MB activation rows of the tile.
 //   x:  LDS double buffer of one group step (64 k = 128 bytes per row), filled by
 //       all waves together; one barrier per group step.
-//   W:  per-wave LDS double buffer of one weight step (128 bytes per row = 256
-//       codes at 4 bits, 128 at 8), requested one weight step ahead; scales and
-//       biases of that step ride along.
-// LDS rows are 128 bytes = 8 chunks of 16; chunk c of row r is stored at chunk
-// c ^ ((r >> 1) & 7), so the 16 rows an MFMA operand read touches fall on 16
-// distinct 16-byte bank groups.
+//   W:  per-wave LDS double buffer of one weight step of 4 groups (128 bytes per
+//       row at 4 bits, 256 at 8), with its scales and biases. Step S+1 is requested
+//       at the first group of step S and written to LDS after its third.
+//   Software pipeline: the B operands (dequantized weights) of group s+1 are
+//       formed while the MFMAs of group s run.
+// Chunk c (16 bytes) of LDS row r is stored at chunk c ^ ((r >> 1) & 7) (8 chunks
+// per row) or c ^ (r & 15) (16 chunks per row), so the 16 rows one MFMA operand
+// read touches fall on 16 distinct 16-byte bank groups.
 //
 // K order (a contraction, so free): in group g, lane group j of an MFMA takes the
-// codes of words 2j + t of the group (4-bit) or 8j + 4t .. of its 16-byte slice
-// (8-bit) at sub-step t, and the A operand the matching 8 activations, which is
-// chunk 2j + t of the activation group in both cases. w = fma(s, q, b) in f32 is
-// rounded to bf16 for the MFMA.
+// codes of word 2j + t of the group (4-bit) or words 4j + 2t, 4j + 2t + 1 (8-bit)
+// at sub-step t, and the A operand the matching 8 activations, which is chunk
+// 2j + t of the activation group in both cases. w = fma(s, q, b) in f32 is rounded
+// to bf16 for the MFMA.
 #pragma once
 
 #include <type_traits>
@@ -36,19 +39,27 @@ struct MmTile2 {
   static constexpr int RW = 16 * NBW;              // weight rows per wave
   static constexpr int BN = RW * WAVES;
   static constexpr int THREADS = 64 * WAVES;
-  static constexpr int GPS = BITS == 4 ? 4 : 2;    // groups per weight step (128 B / row)
+  static constexpr int GPS = 4;                    // groups per weight step
+  static constexpr int ROWB = GPS * 8 * BITS;      // weight bytes per row per step
+  static constexpr int CPR = ROWB / 16;            // 16-byte chunks per row per step
+  static constexpr int RPI = 64 / CPR;             // rows per load instruction
   static constexpr int XBUF = BM * 128;            // bytes per x buffer
-  static constexpr int WBUF = RW * 128;            // bytes per weight buffer (one wave)
-  static constexpr int SBUF = RW * GPS * 2;        // bytes per scale (or bias) buffer
+  static constexpr int WBUF = RW * ROWB;           // bytes per weight buffer (one wave)
+  static constexpr int SEL = RW * GPS;             // scale elements per step
   static constexpr int XINS = BM / 8;              // 1 KB load instructions per x step
-  static constexpr int XPER = (XINS + WAVES - 1) / WAVES;  // per wave (upper bound)
-  static constexpr int WINS = RW / 8;              // 1 KB load instructions per weight step
-  static constexpr int SPL = (RW * GPS + 63) / 64; // scale loads per lane per step
-  static constexpr int PER_WAVE = 2 * WBUF + 4 * SBUF;
+  static constexpr int XPER = (XINS + WAVES - 1) / WAVES;
+  static constexpr int WINS = RW / RPI;            // 1 KB load instructions per weight step
+  static constexpr int SPL = (SEL + 63) / 64;      // scale loads per lane per step
+  static constexpr int PER_WAVE = 2 * WBUF + 4 * SEL * 2;
   static constexpr int LDS_BYTES = 2 * XBUF + WAVES * PER_WAVE;
-  static_assert(BM % 8 == 0 && RW % 8 == 0, "tile rows");
+  static_assert(BM % 8 == 0 && RW % RPI == 0, "tile rows");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 
-  __device__ static __forceinline__ int swz(int r, int c) { return c ^ ((r >> 1) & 7); }
+  __device__ static __forceinline__ int swx(int r, int c) { return c ^ ((r >> 1) & 7); }
+  __device__ static __forceinline__ int sww(int r, int c) {
+    if constexpr (CPR == 8) return c ^ ((r >> 1) & 7);
+    else return c ^ (r & 15);
+  }
 
   __device__ static void run(const uint16_t* __restrict__ x_rows, int rows,
                              const uint32_t* __restrict__ w, const uint16_t* __restrict__ sc,
@@ -66,19 +77,17 @@ struct MmTile2 {
     char* xb = lds;                                   // [2][XBUF]
     char* wv = lds + 2 * XBUF + wave * PER_WAVE;      // this wave's region
     char* wb = wv;                                    // [2][WBUF]
-    uint16_t* sb = reinterpret_cast<uint16_t*>(wv + 2 * WBUF);  // [2][RW*GPS]
-    uint16_t* bb = sb + 2 * RW * GPS;                           // [2][RW*GPS]
+    uint16_t* sb = reinterpret_cast<uint16_t*>(wv + 2 * WBUF);  // [2][SEL]
+    uint16_t* bb = sb + 2 * SEL;                                // [2][SEL]
 
-    // ---- loaders (into registers; the LDS writes come later) ----
-    // x step s (group s): instruction i covers tile rows 8i..8i+7, lane l the 16-byte
-    // chunk at physical slot l % 8 of row 8i + l / 8.
+    // ---- loaders (global -> registers; the LDS writes come later) ----
     u32x4_t xr[XPER];
     auto load_x = [&](int s) {
 #pragma unroll
       for (int k = 0; k < XPER; ++k) {
         const int i = min(wave + k * WAVES, XINS - 1);  // surplus slots re-read (not stored)
         const int r = i * 8 + (lane >> 3);
-        const int c = swz(r, lane & 7);
+        const int c = swx(r, lane & 7);
         const int rr = min(r, rows - 1);
         xr[k] = load_u128(x_rows + (int64_t)rr * K + s * kGroup + c * 8);
       }
@@ -91,18 +100,16 @@ struct MmTile2 {
           *reinterpret_cast<u32x4_t*>(xb + buf * XBUF + i * 1024 + lane * 16) = xr[k];
       }
     };
-    // Weight step S: this wave's rows, 128 bytes each; scales and biases of its GPS
-    // groups.
     const int wrow0 = n0 + wave * RW;
     u32x4_t wr[WINS];
     uint16_t sr[SPL], br[SPL];
     auto load_w = [&](int S) {
 #pragma unroll
       for (int i = 0; i < WINS; ++i) {
-        const int r = i * 8 + (lane >> 3);
-        const int c = swz(r, lane & 7);
+        const int r = i * RPI + lane / CPR;
+        const int c = sww(r, lane % CPR);
         const int n = min(wrow0 + r, N - 1);
-        const int off = min(S * 128 + c * 16, rowbytes - 16);  // last step may be partial
+        const int off = min(S * ROWB + c * 16, rowbytes - 16);  // last step may be partial
         wr[i] = load_stream(reinterpret_cast<const uint32_t*>(
             reinterpret_cast<const char*>(w) + (int64_t)n * rowbytes + off));
       }
@@ -123,46 +130,27 @@ struct MmTile2 {
 #pragma unroll
       for (int h = 0; h < SPL; ++h) {
         const int e = h * 64 + lane;
-        if (e < RW * GPS) {
-          sb[buf * RW * GPS + e] = sr[h];
-          bb[buf * RW * GPS + e] = br[h];
+        if (e < SEL) {
+          sb[buf * SEL + e] = sr[h];
+          bb[buf * SEL + e] = br[h];
         }
       }
     };
 
-    f32x4_t acc[MB][NBW];
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-      for (int nb = 0; nb < NBW; ++nb) acc[mb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-    // ---- prologue: x step 0, weight steps 0 (stored) and 1 (in registers) ----
-    load_w(0);
-    load_x(0);
-    store_w(0);
-    store_x(0);
-    if (nws > 1) load_w(1);
-    __syncthreads();
-
-    for (int s = 0; s < G; ++s) {
-      const int S = s / GPS;
+    // ---- B operands of group s from the weight buffer of its step ----
+    auto dequant = [&](int s, bf16x8_t (&bop)[NBW][2]) {
+      const int wbuf = (s / GPS) & 1;
       const int gs = s % GPS;
-      const int xbuf = s & 1;
-      const int wbuf = S & 1;
-      if (s + 1 < G) load_x(s + 1);
-
-      // B operands: this lane's codes of group s for each of its column blocks.
-      bf16x8_t bop[NBW][2];
 #pragma unroll
       for (int nb = 0; nb < NBW; ++nb) {
         const int r = nb * 16 + ln;
-        const float scale = bf16_to_f32(sb[wbuf * RW * GPS + r * GPS + gs]);
-        const float bias = bf16_to_f32(bb[wbuf * RW * GPS + r * GPS + gs]);
-        const char* row = wb + wbuf * WBUF + r * 128;
+        const float scale = bf16_to_f32(sb[wbuf * SEL + r * GPS + gs]);
+        const float bias = bf16_to_f32(bb[wbuf * SEL + r * GPS + gs]);
+        const char* row = wb + wbuf * WBUF + r * ROWB;
         if constexpr (BITS == 4) {
           // words 2j, 2j+1 of the group: 8 bytes at byte 32 gs + 8 j of the row
           const int c = 2 * gs + (lj >> 1);
-          const uint2 v = *reinterpret_cast<const uint2*>(row + swz(r, c) * 16 + (lj & 1) * 8);
+          const uint2 v = *reinterpret_cast<const uint2*>(row + sww(r, c) * 16 + (lj & 1) * 8);
           const uint32_t wd[2] = {v.x, v.y};
 #pragma unroll
           for (int t = 0; t < 2; ++t) {
@@ -177,7 +165,7 @@ struct MmTile2 {
           }
         } else {
           // words 4j .. 4j+3 of the group: chunk 4 gs + j of the row
-          const u32x4_t v = *reinterpret_cast<const u32x4_t*>(row + swz(r, 4 * gs + lj) * 16);
+          const u32x4_t v = *reinterpret_cast<const u32x4_t*>(row + sww(r, 4 * gs + lj) * 16);
 #pragma unroll
           for (int t = 0; t < 2; ++t) {
             uint32_t d[4];
@@ -193,31 +181,60 @@ struct MmTile2 {
           }
         }
       }
-      // At the first group of a weight step, request the next weight step.
-      if (gs == 0 && S + 1 < nws && s > 0) load_w(S + 1);
+    };
 
-      // A operands and MFMAs.
-      const char* xrow = xb + xbuf * XBUF;
+    f32x4_t acc[MB][NBW];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < NBW; ++nb) acc[mb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    // ---- prologue: x group 0 and weight step 0 in LDS, weight step 1 in registers ----
+    load_w(0);
+    load_x(0);
+    store_w(0);
+    store_x(0);
+    if (nws > 1) load_w(1);
+    __syncthreads();
+    bf16x8_t bop[NBW][2];
+    dequant(0, bop);
+
+    for (int s = 0; s < G; ++s) {
+      const int S = s / GPS;
+      const int gs = s % GPS;
+      const bool more = s + 1 < G;
+      if (more) load_x(s + 1);
+      if (gs == 0 && s > 0 && S + 1 < nws) load_w(S + 1);
+      // Weight step S+1 goes to LDS after the third group of step S, one group
+      // before its first group is dequantized (this wave alone reads it).
+      if (gs == GPS - 2 && S + 1 < nws) store_w((S + 1) & 1);
+
+      // MFMAs of group s; the dequantization of group s+1 is independent of them.
+      const char* xrow = xb + (s & 1) * XBUF;
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
           const int r = mb * 16 + ln;
           const bf16x8_t a = __builtin_bit_cast(
-              bf16x8_t, *reinterpret_cast<const u32x4_t*>(xrow + r * 128 + swz(r, 2 * lj + t) * 16));
+              bf16x8_t, *reinterpret_cast<const u32x4_t*>(xrow + r * 128 + swx(r, 2 * lj + t) * 16));
 #pragma unroll
           for (int nb = 0; nb < NBW; ++nb)
             acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bop[nb][t], acc[mb][nb], 0, 0, 0);
         }
       }
+      bf16x8_t bnext[NBW][2];
+      if (more) dequant(s + 1, bnext);
 
-      // End of a weight step: the next one goes to the other weight buffer (this
-      // wave alone reads it, in order, so no barrier is needed for it).
-      if (gs == GPS - 1 || s + 1 == G) {
-        if (S + 1 < nws) store_w((S + 1) & 1);
-      }
-      if (s + 1 < G) store_x(xbuf ^ 1);
+      if (more) store_x((s & 1) ^ 1);
       __syncthreads();
+      if (more) {
+#pragma unroll
+        for (int nb = 0; nb < NBW; ++nb) {
+          bop[nb][0] = bnext[nb][0];
+          bop[nb][1] = bnext[nb][1];
+        }
+      }
     }
 
     // Epilogue: lane holds rows 4*lj + i of column ln in each 16x16 block.
