@@ -77,4 +77,49 @@ __device__ __forceinline__ float wave_sum_lane63(float v) {
   return v;
 }
 
+// Sum over each aligned group of L lanes (L = 16, 32 or 64), with the same DPP
+// steps: the group's sum ends in its last lane (lane L-1 of the group).
+template <int L>
+__device__ __forceinline__ float lane_group_sum(float v) {
+  static_assert(L == 16 || L == 32 || L == 64, "group width");
+  v = dpp_add<0xB1, 0xF, true>(v);
+  v = dpp_add<0x4E, 0xF, true>(v);
+  v = dpp_add<0x141, 0xF, true>(v);
+  v = dpp_add<0x140, 0xF, true>(v);
+  if constexpr (L >= 32) v = dpp_add<0x142, 0xA, false>(v);
+  if constexpr (L == 64) v = dpp_add<0x143, 0xC, false>(v);
+  return v;
+}
+
+typedef __attribute__((address_space(3))) void lds_ptr_t;
+
+// A pointer every lane of the wave holds, moved to scalar registers.
+template <typename T>
+__device__ __forceinline__ const T* uniform_ptr(const T* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<const T*>(((uint64_t)hi << 32) | lo);
+}
+
+// Buffer descriptor over [base, base + bytes): loads at byte offsets outside it
+// return zeros (checked per dword), so ragged rows need no clamping. The fourth
+// descriptor word is the raw-buffer format of the gfx9 family.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  const int n = (int)min(max(bytes, (int64_t)0), (int64_t)0x7FFFFFFF);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
+}
+
+// Direct HBM -> LDS copy through a descriptor: lane L's SIZE bytes at byte offset
+// voff land at dst + 16 L (SIZE 16) or in the low half of the 4-byte slot dst + 4 L
+// (SIZE 2), without passing through registers.
+template <int SIZE>
+__device__ __forceinline__ void dma(__amdgpu_buffer_rsrc_t r, uint32_t voff, char* dst) {
+  static_assert(SIZE == 16 || SIZE == 2, "copy size");
+  if constexpr (SIZE == 16)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t*)dst, 16, voff, 0, 0, 0);
+  else
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t*)dst, 2, voff, 0, 0, 0);
+}
+
 }  // namespace bitmm

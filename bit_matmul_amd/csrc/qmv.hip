@@ -1,7 +1,10 @@
 // Host side of the GEMV / small-M path (kernel in qmv_impl.hpp).
 #include <stdlib.h>
 
+#include <atomic>
+
 #include "kernels.hpp"
+#include "qmv_dma.hpp"
 #include "qmv_impl.hpp"
 #include "qmv_mfma.hpp"
 
@@ -44,7 +47,30 @@ int forced_path() {
   if (e[0] == 's') return 1;
   if (e[0] == 'v') return 2;
   if (e[0] == 'm') return 3;
+  if (e[0] == 'd') return 4;
   return 0;
+}
+
+// Integer tuning knob from the environment (0 when unset).
+int env_int(const char* name) {
+  const char* e = getenv(name);
+  return e ? atoi(e) : 0;
+}
+
+// Compute units of the current device (cached per device id).
+int compute_units() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    cus = 256;
+  if (dev < 64) cache[dev].store(cus, std::memory_order_relaxed);
+  return cus;
 }
 
 }  // namespace
@@ -87,6 +113,22 @@ hipError_t launch_qmv(const uint16_t* x, const uint32_t* w, const uint16_t* scal
       mp.out_f32 = p.out_f32;
       e = bits == 4 ? qmv_detail::launch_mfma_bits<4>(mp, mr, sk, stream)
                     : qmv_detail::launch_mfma_bits<8>(mp, mr, sk, stream);
+    } else if ((path == 0 || path == 4) && mr == 1 &&
+               qmv_dma_detail::pick_lanes(nch) != 0) {
+      qmv_dma_detail::Params dp;
+      dp.x = p.x;
+      dp.w = w;
+      dp.s = scales;
+      dp.b = biases;
+      dp.y = p.y;
+      dp.N = (int)N;
+      dp.K = (int)K;
+      dp.out_f32 = p.out_f32;
+      dp.steps_per_wave = dp.total_steps = 0;
+      const int cus = compute_units();
+      const int wpc = env_int("BITMM_QMV_WAVES_PER_CU");
+      e = bits == 4 ? qmv_dma_detail::launch_bits<4>(dp, cus, wpc, stream)
+                    : qmv_dma_detail::launch_bits<8>(dp, cus, wpc, stream);
     } else if ((path == 0 || path == 1) && mr == 1 && cpl_all <= 5) {
       const int rpw = stream_rows_per_wave(N);
       e = bits == 4 ? qmv_detail::launch_stream_bits<4>(p, (int)cpl_all, rpw, stream)

@@ -1,0 +1,300 @@
+// Decode GEMV, y[n] = sum_k x[k] (s[n][g] q[n][k] + b[n][g]) for one activation row,
+// built around the HBM stream.
+//
+// A step is R = 64 / L consecutive weight rows; lane l works on row l / L of the
+// step and, within it, on the 16-byte code chunks (l % L) + L*m, m < C. A lane's
+// chunks are the same in every step, and the R rows of a step are one contiguous
+// span of W, fetched by C loads of 1 KB per wave (the fastest HBM access shape).
+//
+// Each wave owns consecutive steps and keeps a ring of five in registers: the
+// loads of step i+4 are issued before step i is computed, so four steps (about
+// 20 KB at K = 5120) are in flight per wave. The activations (the same for every
+// row) are prepared once per workgroup in LDS and then held in registers. Loads go through buffer descriptors
+// over the rows that exist: rows past N, and chunks past the end of a row, read as
+// zeros (their scale and bias too, so they add nothing).
+//
+// Arithmetic per chunk, the affine split (all codes of a chunk share a group):
+//   sum_k x_k (s q_k + b) = s * sum_k x_k q_k + b * sum_k x_k.
+// 4-bit: a nibble pair masked into 0x4300 is the exact bf16 pair (128+q_j, 128+q_{j+4});
+// v_dot2_f32_bf16 against the matching activation pair gives P = sum x (128 + q),
+// then s*P + (b - 128 s) * sum x. 8-bit: codes convert to f32 byte by byte.
+// Products are exact in f32 and accumulation is f32 (the decode fix of epic #1536,
+// diagnosis item 3: accumulate the 4-bit GEMV in float).
+#pragma once
+
+#include "common.hpp"
+
+namespace bitmm {
+namespace qmv_dma_detail {
+
+struct Params {
+  const uint16_t* x;
+  const uint32_t* w;
+  const uint16_t* s;
+  const uint16_t* b;
+  void* y;
+  int N, K;
+  int out_f32;
+  int steps_per_wave;  // consecutive steps each wave owns
+  int total_steps;     // ceil(N / R)
+};
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / kWave;
+constexpr int kWavesPerCu = 8;  // launch target; the kernel holds one or two waves per SIMD
+
+template <int BITS, int L, int C, int SPW>
+struct Cfg {
+  static constexpr int R = 64 / L;       // rows per step
+  static constexpr int CC = 128 / BITS;  // codes per 16-byte chunk
+  static constexpr int LOADS = 3 * C;    // load instructions per step (codes, scales, biases)
+  static constexpr int D = SPW < 5 ? SPW : 5;  // steps in flight at once (at most 4 ahead)
+  static constexpr int XCH = 64 * C;     // activation chunks held in LDS (covers L * C)
+  // Activations per chunk in LDS: 4-bit 16 bf16 pairs matched to nibble pairs (64 B);
+  // 8-bit 16 f32 (64 B). Stored as 4 planes of 16 bytes, plane u of chunk c at
+  // (u * XCH + c) * 16, so the 64 lanes' reads of one plane are contiguous.
+  static constexpr int X_BYTES = 4 * XCH * 16;
+  static constexpr int LDS_BYTES = X_BYTES + XCH * 4;  // + per-chunk activation sums
+};
+
+// Cache-policy operand of a buffer load: non-temporal (the codes are read once).
+constexpr int kNonTemporal = 2;
+
+// Byte offset outside every descriptor: such a load reads zeros.
+constexpr uint32_t kNoChunk = 0x80000000u;
+
+template <int BITS, int L, int C, int SPW>
+__global__ __launch_bounds__(kThreads) void qmv_dma_kernel(Params p) {
+  using T = Cfg<BITS, L, C, SPW>;
+  __shared__ __attribute__((aligned(16))) char lds[T::LDS_BYTES];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int step0 = (blockIdx.x * kWaves + wave) * SPW;
+  const bool active = step0 < p.total_steps;  // uniform per wave
+  const int slast = active ? min(step0 + SPW, p.total_steps) - 1 : p.total_steps - 1;
+  const int N = p.N, K = p.K;
+  const int nch = K / T::CC;          // chunks per row
+  const int G = K / kGroup;
+  const int64_t rowbytes = (int64_t)K * BITS / 8;
+  const int r = lane / L;             // row of the step
+  const int li = lane % L;
+  const uint32_t* wq = uniform_ptr(p.w);
+  const uint16_t* sq = uniform_ptr(p.s);
+  const uint16_t* bq = uniform_ptr(p.b);
+
+  // Per-lane byte offsets of the lane's chunks, relative to the step's first row.
+  uint32_t coff[C], soff[C];
+#pragma unroll
+  for (int m = 0; m < C; ++m) {
+    const int c = li + L * m;
+    const bool ok = c < nch;
+    coff[m] = ok ? (uint32_t)(r * rowbytes + c * 16) : kNoChunk;
+    soff[m] = ok ? (uint32_t)((r * G + c * T::CC / kGroup) * 2) : kNoChunk;
+  }
+  struct Step {
+    u32x4_t q[C];
+    uint32_t s[C], b[C];
+  };
+  auto load_step = [&](int step, Step& S) {
+    const int64_t row0 = (int64_t)step * T::R;
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(reinterpret_cast<const char*>(wq) + row0 * rowbytes,
+                                                (N - row0) * rowbytes);
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(sq + row0 * G, (N - row0) * G * 2);
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(bq + row0 * G, (N - row0) * G * 2);
+#pragma unroll
+    for (int m = 0; m < C; ++m)
+      S.q[m] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rw, coff[m], 0, kNonTemporal));
+#pragma unroll
+    for (int m = 0; m < C; ++m) S.s[m] = __builtin_amdgcn_raw_buffer_load_b16(rs, soff[m], 0, 0);
+#pragma unroll
+    for (int m = 0; m < C; ++m) S.b[m] = __builtin_amdgcn_raw_buffer_load_b16(rb, soff[m], 0, 0);
+  };
+
+  // Activations, once per workgroup: thread t prepares chunks t, t + 256, ... (zero
+  // past the row end) into LDS; each lane then copies its own C chunks into
+  // registers for the whole kernel. Their loads are issued first, so waiting for
+  // them never waits for weight loads (loads retire in order).
+  constexpr int XPT = (T::XCH + kThreads - 1) / kThreads;  // chunks per thread
+  constexpr int XU = BITS == 4 ? 4 : 2;                     // 16-byte activation loads per chunk
+  u32x4_t xin[XPT][XU];
+#pragma unroll
+  for (int j = 0; j < XPT; ++j) {
+    const int c = threadIdx.x + j * kThreads;
+    const bool ok = c < nch;
+#pragma unroll
+    for (int u = 0; u < XU; ++u) xin[j][u] = load_u128(p.x + (int64_t)(ok ? c : 0) * T::CC + 8 * u);
+  }
+
+  __builtin_amdgcn_sched_barrier(0);  // activation loads first: they retire first
+  // The wave's SPW steps are straight-line code: the loads of step i+D-1 go out
+  // before step i is computed (past the wave's last step they repeat that step, an
+  // L2 hit), so the number of loads in flight at every wait is known exactly. A
+  // wave without steps loads a valid step too, to keep the prologue branch-free.
+  Step ring[SPW];
+#pragma unroll
+  for (int i = 0; i < T::D - 1; ++i) load_step(min(step0 + i, slast), ring[i]);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int j = 0; j < XPT; ++j) {
+    const int c = threadIdx.x + j * kThreads;
+    if (c >= T::XCH) break;
+    const bool ok = c < nch;
+    uint32_t raw[BITS == 4 ? 16 : 8];
+#pragma unroll
+    for (int u = 0; u < XU; ++u)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) raw[4 * u + e] = ok ? xin[j][u][e] : 0u;
+    float t = 0.f;
+#pragma unroll
+    for (int d = 0; d < 4 * XU; ++d) t = dot2_bf16(raw[d], 0x3F803F80u, t);
+    reinterpret_cast<float*>(lds + T::X_BYTES)[c] = t;
+    uint32_t out[16];
+    if constexpr (BITS == 4) {
+      // code word wd holds codes 8 wd .. 8 wd + 7; nibble pair (j, j+4) meets the
+      // activation pair (x_{8wd+j}, x_{8wd+j+4}).
+#pragma unroll
+      for (int wd = 0; wd < 4; ++wd) {
+        const uint32_t d0 = raw[4 * wd], d1 = raw[4 * wd + 1], d2 = raw[4 * wd + 2], d3 = raw[4 * wd + 3];
+        out[4 * wd + 0] = perm_b32(d2, d0, 0x05040100u);
+        out[4 * wd + 1] = perm_b32(d2, d0, 0x07060302u);
+        out[4 * wd + 2] = perm_b32(d3, d1, 0x05040100u);
+        out[4 * wd + 3] = perm_b32(d3, d1, 0x07060302u);
+      }
+    } else {
+#pragma unroll
+      for (int d = 0; d < 8; ++d) {
+        out[2 * d] = raw[d] << 16;             // f32 bits of the low bf16
+        out[2 * d + 1] = raw[d] & 0xFFFF0000u;  // f32 bits of the high bf16
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      *reinterpret_cast<u32x4_t*>(lds + (u * T::XCH + c) * 16) =
+          u32x4_t{out[4 * u], out[4 * u + 1], out[4 * u + 2], out[4 * u + 3]};
+  }
+  __syncthreads();
+  if (!active) return;
+  u32x4_t xr[C][4];
+  float sx[C];
+#pragma unroll
+  for (int m = 0; m < C; ++m) {
+    const int c = li + L * m;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) xr[m][u] = *reinterpret_cast<const u32x4_t*>(lds + (u * T::XCH + c) * 16);
+    sx[m] = reinterpret_cast<const float*>(lds + T::X_BYTES)[c];
+  }
+
+  const uint32_t magic = 0x43004300u;  // bf16 pair (128, 128)
+  auto compute = [&](int step, const Step& S) {
+    float acc = 0.f;
+#pragma unroll
+    for (int m = 0; m < C; ++m) {
+      const float s = __uint_as_float(S.s[m] << 16);
+      const float b = __uint_as_float(S.b[m] << 16);
+      float P[4] = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (BITS == 4) {
+#pragma unroll
+        for (int wd = 0; wd < 4; ++wd)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            P[j] = dot2_bf16(and_or_b32(S.q[m][wd] >> (4 * j), 0x000F000Fu, magic), xr[m][wd][j], P[j]);
+        const float Pt = (P[0] + P[1]) + (P[2] + P[3]);
+        acc = fmaf(s, Pt, fmaf(fmaf(-128.f, s, b), sx[m], acc));
+      } else {
+#pragma unroll
+        for (int wd = 0; wd < 4; ++wd)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            P[j] = fmaf(__uint_as_float(xr[m][wd][j]), (float)((S.q[m][wd] >> (8 * j)) & 0xFFu), P[j]);
+        const float Pt = (P[0] + P[1]) + (P[2] + P[3]);
+        acc = fmaf(s, Pt, fmaf(b, sx[m], acc));
+      }
+    }
+    const float v = lane_group_sum<L>(acc);
+    const int n = step * T::R + r;
+    if (li == L - 1 && n < N) {
+      if (p.out_f32)
+        static_cast<float*>(p.y)[n] = v;
+      else
+        static_cast<uint16_t*>(p.y)[n] = f32_to_bf16(v);
+    }
+  };
+
+#pragma unroll
+  for (int i = 0; i < SPW; ++i) {
+    if (i + T::D - 1 < SPW) load_step(min(step0 + i + T::D - 1, slast), ring[i + T::D - 1]);
+    if (step0 + i > slast) break;  // uniform: the wave's last step is done
+    compute(step0 + i, ring[i]);
+  }
+}
+
+// Chunk layout for K (0 if this kernel does not take it): lanes per row L and
+// chunks per lane C <= 5, the fewest idle chunk slots, ties to more lanes per row.
+inline int pick_lanes(int64_t nch) {
+  int best = 0;
+  int64_t waste = 1 << 30;
+  for (int L : {64, 32, 16}) {
+    const int64_t c = (nch + L - 1) / L;
+    if (c < 1 || c > 5) continue;
+    const int64_t w = c * L - nch;
+    if (w < waste) {
+      waste = w;
+      best = L;
+    }
+  }
+  return best;
+}
+
+template <int BITS, int L, int C, int SPW>
+hipError_t launch(Params p, hipStream_t stream) {
+  using T = Cfg<BITS, L, C, SPW>;
+  p.total_steps = (p.N + T::R - 1) / T::R;
+  p.steps_per_wave = SPW;
+  const int waves = (p.total_steps + SPW - 1) / SPW;
+  const int blocks = (waves + kWaves - 1) / kWaves;
+  hipLaunchKernelGGL((qmv_dma_kernel<BITS, L, C, SPW>), dim3(blocks), dim3(kThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+// Steps per wave: the largest of 8, 4, 2, 1 that still gives every SIMD of the chip
+// at least `waves_per_cu` / 4 waves.
+template <int BITS, int L, int C>
+hipError_t launch_spw(const Params& p, int cus, int waves_per_cu, hipStream_t stream) {
+  const int64_t steps = (p.N + (64 / L) - 1) / (64 / L);
+  const int64_t want = (int64_t)cus * waves_per_cu;
+  if (steps >= want * 8) return launch<BITS, L, C, 8>(p, stream);
+  if (steps >= want * 4) return launch<BITS, L, C, 4>(p, stream);
+  if (steps >= want * 2) return launch<BITS, L, C, 2>(p, stream);
+  return launch<BITS, L, C, 1>(p, stream);
+}
+
+template <int BITS, int L>
+hipError_t launch_c(const Params& p, int c, int cus, int wpc, hipStream_t stream) {
+  switch (c) {
+    case 1: return launch_spw<BITS, L, 1>(p, cus, wpc, stream);
+    case 2: return launch_spw<BITS, L, 2>(p, cus, wpc, stream);
+    case 3: return launch_spw<BITS, L, 3>(p, cus, wpc, stream);
+    case 4: return launch_spw<BITS, L, 4>(p, cus, wpc, stream);
+    default: return launch_spw<BITS, L, 5>(p, cus, wpc, stream);
+  }
+}
+
+// Returns hipErrorNotSupported when K has more than 5 chunks per lane.
+template <int BITS>
+hipError_t launch_bits(const Params& p, int cus, int wpc, hipStream_t stream) {
+  const int64_t nch = (int64_t)p.K * BITS / 128;
+  const int L = pick_lanes(nch);
+  if (L == 0) return hipErrorNotSupported;
+  const int c = (int)((nch + L - 1) / L);
+  if (wpc <= 0) wpc = kWavesPerCu;
+  if (L == 64) return launch_c<BITS, 64>(p, c, cus, wpc, stream);
+  if (L == 32) return launch_c<BITS, 32>(p, c, cus, wpc, stream);
+  return launch_c<BITS, 16>(p, c, cus, wpc, stream);
+}
+
+}  // namespace qmv_dma_detail
+
+extern template hipError_t qmv_dma_detail::launch_bits<4>(const qmv_dma_detail::Params&, int, int, hipStream_t);
+extern template hipError_t qmv_dma_detail::launch_bits<8>(const qmv_dma_detail::Params&, int, int, hipStream_t);
+
+}  // namespace bitmm

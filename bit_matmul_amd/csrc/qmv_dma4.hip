@@ -1,0 +1,6 @@
+// 4-bit instantiations of the LDS-ring GEMV.
+#include "qmv_dma.hpp"
+
+namespace bitmm {
+template hipError_t qmv_dma_detail::launch_bits<4>(const qmv_dma_detail::Params&, int, int, hipStream_t);
+}  // namespace bitmm

@@ -51,7 +51,7 @@ def test_qmv_small(M, N, K, bits, out):
     G.assert_close(got, oracle_dense(d), out, f"qmv M{M} N{N} K{K} b{bits}")
 
 
-@pytest.mark.parametrize("path", ["stream", "valu", "mfma"])
+@pytest.mark.parametrize("path", ["dma", "stream", "valu", "mfma"])
 @pytest.mark.parametrize("bits", [4, 8])
 @pytest.mark.parametrize("M,N,K", [(1, 300, 640), (1, 64, 8256), (1, 33, 192), (3, 130, 5120),
                                    (8, 40, 576)])
@@ -62,6 +62,21 @@ def test_qmv_every_kernel(M, N, K, bits, path, monkeypatch):
     d = I.random_dense(M, N, K, bits, seed=11 * M + N + K)
     got = G.to_f64(G.run_dense("bitmm_qmv", d, "f32"))
     G.assert_close(got, oracle_dense(d), "f32", f"qmv[{path}] M{M} N{N} K{K} b{bits}")
+
+
+# The LDS-ring GEMV at its layout edges: one row; R-row steps with a ragged last
+# step (N odd, N = 4k+1); idle chunk slots (K/chunk not a multiple of lanes per
+# row); 16, 32 and 64 lanes per row; 1 to 5 chunks per lane (K up to 10240 at 4
+# bits, 5120 at 8 bits); N smaller and larger than the number of waves.
+@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("out", ["bf16", "f32"])
+@pytest.mark.parametrize("N,K", [(1, 64), (5, 5120), (4099, 5120), (257, 512), (33, 192),
+                                 (2048, 10240), (100, 2816), (3001, 1344)])
+def test_qmv_dma_layouts(N, K, bits, out, monkeypatch):
+    monkeypatch.setenv("BITMM_QMV_PATH", "dma")
+    d = I.random_dense(1, N, K, bits, seed=N + 3 * K + bits)
+    got = G.to_f64(G.run_dense("bitmm_qmv", d, out))
+    G.assert_close(got, oracle_dense(d), out, f"qmv[dma] N{N} K{K} b{bits}")
 
 
 @pytest.mark.parametrize("bits", [4, 8])
