@@ -22,6 +22,7 @@ hot path (the 8-bit GEMV, the prefill GEMM at M = 600 and M = 3, 4- and 8-bit,
 and the MoE expert-gathered GEMM in both orientations), timed the same way.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-suite] [--no-cpu]
+                       [--calibrate-copy]
 """
 
 from __future__ import annotations
@@ -194,6 +195,9 @@ def main():
     ap.add_argument("--no-suite", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a 256 MiB device-to-device copy 5 times: the reference "
+                         "for scaling the FETCH_SIZE / WRITE_SIZE counters to bytes")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -230,7 +234,8 @@ def main():
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": read_traffic("qmv_K5120_N13824_b4_traffic", src_hash),
-                "kernel": "qmv_mfma_kernel<4,1,4> (K=5120, N=13824, 4-bit, M=1)",
+                "kernel": "qmv_dma_kernel<4, 32, 5, *> (K=5120, N=13824, 4-bit, M=1: steps of "
+                          "2 rows x 32 lanes x 5 chunks)",
                 "algorithmic_bytes_per_launch": cb.bytes,
                 "avg_launch_us": round(tb * 1e6, 3)}
 
@@ -258,6 +263,17 @@ def main():
     }
     del ca, cb
     torch.cuda.empty_cache()
+
+    if args.calibrate_copy:
+        n = 256 << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        result["calibration_copy_bytes"] = n
+        del src, dst
+        torch.cuda.empty_cache()
 
     # ---- the rest of the hot path ------------------------------------------
     if not args.no_suite:
