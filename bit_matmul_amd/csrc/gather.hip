@@ -12,11 +12,7 @@
 //      row range from the workspace and runs the shared matrix-core tile over those
 //      rows, so each expert's codes are streamed once per column block however many
 //      rows the expert has. Experts without rows exit at once.
-#include <stdlib.h>
-
 #include "kernels.hpp"
-#include "mfma_tile.hpp"
-#include "mfma_tile2.hpp"
 #include "mfma_tile3.hpp"
 
 namespace bitmm {
@@ -130,12 +126,6 @@ hipError_t launch_grouped(GatherParams p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-int tile_form() {
-  const char* e = getenv("BITMM_MM_TILE");
-  if (e && (e[0] == '1' || e[0] == '2')) return e[0] - '0';
-  return 3;
-}
-
 // Pipelined tile, one row of 4 waves (each expert's weights dequantized once per
 // row block). Row blocks of 16 per tile from the mean rows per expert, with slack for
 // the spread of the routing: experts with more rows loop over row tiles.
@@ -178,14 +168,6 @@ hipError_t launch_gather_qmm(const uint16_t* x, const uint32_t* w, const uint16_
   p.E = (int)E;
   p.tiles_n = 0;
   p.out_f32 = out_f32 ? 1 : 0;
-  if (tile_form() == 1) {
-    if (bits == 4) return launch_grouped<4, MmTile<4, 4, 2, 4>>(p, stream);
-    return launch_grouped<8, MmTile<8, 4, 2, 4>>(p, stream);
-  }
-  if (tile_form() == 2) {
-    if (bits == 4) return launch_grouped<4, MmTile2<4, 4, 2, 4>>(p, stream);
-    return launch_grouped<8, MmTile2<8, 4, 2, 4>>(p, stream);
-  }
   return bits == 4 ? launch_tile3<4>(p, stream) : launch_tile3<8>(p, stream);
 }
 

@@ -1,11 +1,7 @@
 // Dense prefill GEMM on the matrix cores (M >= 8): y[M, N] = x[M, K] * dequant(w)^T.
 // The epic's kernel table puts the prefill quantized GEMM at 82% of GPU time; the
-// tile itself lives in mfma_tile.hpp.
-#include <stdlib.h>
-
+// tile itself lives in mfma_tile3.hpp.
 #include "kernels.hpp"
-#include "mfma_tile.hpp"
-#include "mfma_tile2.hpp"
 #include "mfma_tile3.hpp"
 
 namespace bitmm {
@@ -54,39 +50,6 @@ hipError_t launch_tiles(QmmParams p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Tile form: 3 = pipelined 2x2-wave tile (default), 2 = one-wave-column LDS tile,
-// 1 = weights straight to registers. BITMM_MM_TILE selects one (comparison knob).
-int tile_form() {
-  const char* e = getenv("BITMM_MM_TILE");
-  if (e && (e[0] == '1' || e[0] == '2')) return e[0] - '0';
-  return 3;
-}
-
-// Row blocks of 16 per tile: as few row tiles as the LDS budget allows (at most 20
-// blocks, 320 rows), each as full as possible, so every dequantized weight feeds as
-// many MFMA row blocks as the batch has.
-int row_blocks(int64_t M) {
-  const int64_t blocks = (M + 15) / 16;
-  const int64_t tiles = (blocks + 19) / 20;
-  const int64_t need = (blocks + tiles - 1) / tiles;
-  if (need <= 4) return 4;
-  if (need <= 8) return 8;
-  if (need <= 12) return 12;
-  if (need <= 16) return 16;
-  return 20;
-}
-
-template <int BITS>
-hipError_t launch_bits(QmmParams p, hipStream_t stream) {
-  switch (row_blocks(p.M)) {
-    case 4: return launch_tiles<MmTile2<BITS, 4, 2, 4>>(p, stream);
-    case 8: return launch_tiles<MmTile2<BITS, 8, 2, 4>>(p, stream);
-    case 12: return launch_tiles<MmTile2<BITS, 12, 2, 4>>(p, stream);
-    case 16: return launch_tiles<MmTile2<BITS, 16, 2, 4>>(p, stream);
-    default: return launch_tiles<MmTile2<BITS, 20, 2, 4>>(p, stream);
-  }
-}
-
 // Pipelined tile: one row of 4 waves, each with 32 weight rows (columns of y) and
 // all the tile's activation rows, so a weight is dequantized once per row tile.
 // As few row tiles as fit in LDS (at most 320 rows), each as full as possible.
@@ -124,11 +87,6 @@ hipError_t launch_qmm_mfma(const uint16_t* x, const uint32_t* w, const uint16_t*
   p.K = (int)K;
   p.out_f32 = out_f32 ? 1 : 0;
   p.tiles_m = p.tiles_n = 0;
-  if (tile_form() == 1) {
-    if (bits == 4) return launch_tiles<MmTile<4, 8, 2, 4>>(p, stream);
-    return launch_tiles<MmTile<8, 8, 2, 4>>(p, stream);
-  }
-  if (tile_form() == 2) return bits == 4 ? launch_bits<4>(p, stream) : launch_bits<8>(p, stream);
   return bits == 4 ? launch_tile3<4>(p, stream) : launch_tile3<8>(p, stream);
 }
 

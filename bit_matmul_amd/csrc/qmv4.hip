@@ -4,6 +4,4 @@
 namespace bitmm {
 template hipError_t qmv_detail::launch_bits<4>(const qmv_detail::QmvParams&, int, int,
                                                 hipStream_t);
-template hipError_t qmv_detail::launch_stream_bits<4>(const qmv_detail::QmvParams&, int, int,
-                                                       hipStream_t);
 }  // namespace bitmm

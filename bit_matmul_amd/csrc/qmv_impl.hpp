@@ -207,152 +207,6 @@ __global__ __launch_bounds__(kQmvThreads) void qmv_kernel(QmvParams p) {
   }
 }
 
-// ---------------------------------------------------------------------------
-// Decode GEMV (M = 1), streaming form. Lane l owns the 16-byte chunks
-// l, l+64, ... (at most CPL of them) of EVERY row, so its activation chunks are
-// loaded, rearranged and summed once per wave and stay in registers. The wave
-// then walks a block of `rpw` consecutive rows with a ring of three row buffers:
-// the loads of row n+2 are issued before row n is computed, so two rows of
-// codes are in flight behind the arithmetic. Each row ends with a DPP reduction.
-// ---------------------------------------------------------------------------
-template <int BITS, int CPL>
-__global__ __launch_bounds__(kQmvThreads) void qmv_stream_kernel(QmvParams p, int rpw) {
-  constexpr int CC = 128 / BITS;
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = blockIdx.x * kQmvWaves + (threadIdx.x >> 6);
-  const int nfirst = wave * rpw;
-  if (nfirst >= p.N) return;  // uniform per wave
-  const int nend = min(nfirst + rpw, p.N);
-  const int nch = p.K / CC;
-  const int G = p.K / kGroup;
-  const int64_t wrow = (int64_t)p.K * BITS / 32;
-
-  int cidx[CPL], gidx[CPL];
-  bool ok[CPL];
-#pragma unroll
-  for (int i = 0; i < CPL; ++i) {
-    const int c = i * kWave + lane;
-    ok[i] = c < nch;
-    cidx[i] = ok[i] ? c : nch - 1;
-    gidx[i] = cidx[i] * CC / kGroup;
-  }
-
-  // Activations, once per wave.
-  constexpr int XD = CC / 2;  // activation dwords (bf16 pairs) per chunk
-  uint32_t xraw[CPL][XD];
-#pragma unroll
-  for (int i = 0; i < CPL; ++i) {
-#pragma unroll
-    for (int u = 0; u < XD / 4; ++u) {
-      const u32x4_t v = load_u128(p.x + (int64_t)cidx[i] * CC + 8 * u);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) xraw[i][4 * u + e] = ok[i] ? v[e] : 0u;
-    }
-  }
-  float sx[CPL];
-  // 4-bit: activation pairs (x_j, x_{j+4}) of each word; 8-bit: f32 activations.
-  uint32_t xp[BITS == 4 ? CPL : 1][4][4];
-  float xf[BITS == 8 ? CPL : 1][16];
-#pragma unroll
-  for (int i = 0; i < CPL; ++i) {
-    float t = 0.f;
-#pragma unroll
-    for (int d = 0; d < XD; ++d) t = dot2_bf16(xraw[i][d], 0x3F803F80u, t);
-    sx[i] = t;
-    if constexpr (BITS == 4) {
-#pragma unroll
-      for (int wd = 0; wd < 4; ++wd) {
-        const uint32_t d0 = xraw[i][4 * wd], d1 = xraw[i][4 * wd + 1];
-        const uint32_t d2 = xraw[i][4 * wd + 2], d3 = xraw[i][4 * wd + 3];
-        xp[i][wd][0] = perm_b32(d2, d0, 0x05040100u);  // (x0, x4)
-        xp[i][wd][1] = perm_b32(d2, d0, 0x07060302u);  // (x1, x5)
-        xp[i][wd][2] = perm_b32(d3, d1, 0x05040100u);  // (x2, x6)
-        xp[i][wd][3] = perm_b32(d3, d1, 0x07060302u);  // (x3, x7)
-      }
-    } else {
-#pragma unroll
-      for (int d = 0; d < 8; ++d) {
-        xf[i][2 * d] = bf16_lo(xraw[i][d]);
-        xf[i][2 * d + 1] = bf16_hi(xraw[i][d]);
-      }
-    }
-  }
-
-  struct Row {
-    u32x4_t q[CPL];
-    uint16_t s[CPL], b[CPL];
-  };
-  auto load_row = [&](int n, Row& R) {
-    const uint32_t* wr = p.w + (int64_t)n * wrow;
-    const uint16_t* sr = p.s + (int64_t)n * G;
-    const uint16_t* br = p.b + (int64_t)n * G;
-#pragma unroll
-    for (int i = 0; i < CPL; ++i) {
-      R.q[i] = load_stream(wr + 4 * (int64_t)cidx[i]);
-      R.s[i] = sr[gidx[i]];
-      R.b[i] = br[gidx[i]];
-    }
-  };
-  const uint32_t magic = 0x43004300u;  // bf16 pair (128, 128)
-  auto compute_row = [&](int n, const Row& R) {
-    float acc = 0.f;
-#pragma unroll
-    for (int i = 0; i < CPL; ++i) {
-      const float s = bf16_to_f32(R.s[i]);
-      const float b = bf16_to_f32(R.b[i]);
-      if constexpr (BITS == 4) {
-        float P[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int wd = 0; wd < 4; ++wd) {
-          const uint32_t w0 = R.q[i][wd];
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            P[j] = dot2_bf16(and_or_b32(w0 >> (4 * j), 0x000F000Fu, magic), xp[i][wd][j], P[j]);
-        }
-        const float Pt = (P[0] + P[1]) + (P[2] + P[3]);
-        acc = fmaf(s, Pt, fmaf(fmaf(-128.f, s, b), sx[i], acc));
-      } else {
-        float P[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int wd = 0; wd < 4; ++wd) {
-          const uint32_t w0 = R.q[i][wd];
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            P[j] = fmaf(xf[i][4 * wd + j], (float)((w0 >> (8 * j)) & 0xFFu), P[j]);
-        }
-        const float Pt = (P[0] + P[1]) + (P[2] + P[3]);
-        acc = fmaf(s, Pt, fmaf(b, sx[i], acc));
-      }
-    }
-    const float v = wave_sum_lane63(acc);
-    if (lane == kWave - 1 && n < nend) {
-      if (p.out_f32)
-        static_cast<float*>(p.y)[n] = v;
-      else
-        static_cast<uint16_t*>(p.y)[n] = f32_to_bf16(v);
-    }
-  };
-
-  // Every load is unconditional: past the wave's last row the row index clamps to
-  // that row (an L2 hit, never another wave's row), so the compiler can count
-  // outstanding loads exactly and wait only for the row it is about to use.
-  const int nlast = nend - 1;
-  Row ring[3];
-  load_row(nfirst, ring[0]);
-  load_row(min(nfirst + 1, nlast), ring[1]);
-  for (int n = nfirst; n < nend; n += 3) {
-    load_row(min(n + 2, nlast), ring[2]);
-    __builtin_amdgcn_sched_barrier(0);
-    compute_row(n, ring[0]);
-    load_row(min(n + 3, nlast), ring[0]);
-    __builtin_amdgcn_sched_barrier(0);
-    compute_row(n + 1, ring[1]);
-    load_row(min(n + 4, nlast), ring[1]);
-    __builtin_amdgcn_sched_barrier(0);
-    compute_row(n + 2, ring[2]);
-  }
-}
-
 template <int BITS, int MR, int RPW, int CPL>
 hipError_t launch_one(const QmvParams& p, hipStream_t stream) {
   const int waves = (p.N + RPW - 1) / RPW;
@@ -380,29 +234,6 @@ hipError_t pick_cpl(const QmvParams& p, int cpl, hipStream_t stream) {
   }
 }
 
-template <int BITS, int CPL>
-hipError_t launch_stream(const QmvParams& p, int rpw, hipStream_t stream) {
-  const int waves = (p.N + rpw - 1) / rpw;
-  const int blocks = (waves + kQmvWaves - 1) / kQmvWaves;
-  hipLaunchKernelGGL((qmv_stream_kernel<BITS, CPL>), dim3(blocks), dim3(kQmvThreads), 0, stream, p,
-                     rpw);
-  return hipGetLastError();
-}
-
-// Streaming form: M = 1 with every chunk of a row covered in one pass
-// (chunks per lane <= 5). Returns hipErrorNotSupported otherwise.
-template <int BITS>
-hipError_t launch_stream_bits(const QmvParams& p, int cpl, int rpw, hipStream_t stream) {
-  switch (cpl) {
-    case 1: return launch_stream<BITS, 1>(p, rpw, stream);
-    case 2: return launch_stream<BITS, 2>(p, rpw, stream);
-    case 3: return launch_stream<BITS, 3>(p, rpw, stream);
-    case 4: return launch_stream<BITS, 4>(p, rpw, stream);
-    case 5: return launch_stream<BITS, 5>(p, rpw, stream);
-    default: return hipErrorNotSupported;
-  }
-}
-
 template <int BITS>
 hipError_t launch_bits(const QmvParams& p, int mr, int cpl, hipStream_t stream) {
   switch (mr) {
@@ -422,7 +253,5 @@ hipError_t launch_bits(const QmvParams& p, int mr, int cpl, hipStream_t stream) 
 // One explicit instantiation per bit width, each in its own translation unit.
 extern template hipError_t qmv_detail::launch_bits<4>(const qmv_detail::QmvParams&, int, int, hipStream_t);
 extern template hipError_t qmv_detail::launch_bits<8>(const qmv_detail::QmvParams&, int, int, hipStream_t);
-extern template hipError_t qmv_detail::launch_stream_bits<4>(const qmv_detail::QmvParams&, int, int, hipStream_t);
-extern template hipError_t qmv_detail::launch_stream_bits<8>(const qmv_detail::QmvParams&, int, int, hipStream_t);
 
 }  // namespace bitmm

@@ -51,12 +51,13 @@ def test_qmv_small(M, N, K, bits, out):
     G.assert_close(got, oracle_dense(d), out, f"qmv M{M} N{N} K{K} b{bits}")
 
 
-@pytest.mark.parametrize("path", ["dma", "stream", "valu", "mfma"])
+@pytest.mark.parametrize("path", ["auto", "valu"])
 @pytest.mark.parametrize("bits", [4, 8])
 @pytest.mark.parametrize("M,N,K", [(1, 300, 640), (1, 64, 8256), (1, 33, 192), (3, 130, 5120),
                                    (8, 40, 576)])
 def test_qmv_every_kernel(M, N, K, bits, path, monkeypatch):
-    """Each GEMV kernel form (chosen with the BITMM_QMV_PATH knob) against the oracle,
+    """Both GEMV kernel forms (the one-row LDS-staged kernel where it applies, and the
+    general small-M kernel forced with the BITMM_QMV_PATH knob) against the oracle,
     f32 output, where the exact-product rule applies."""
     monkeypatch.setenv("BITMM_QMV_PATH", path)
     d = I.random_dense(M, N, K, bits, seed=11 * M + N + K)
@@ -73,7 +74,7 @@ def test_qmv_every_kernel(M, N, K, bits, path, monkeypatch):
 @pytest.mark.parametrize("N,K", [(1, 64), (5, 5120), (4099, 5120), (257, 512), (33, 192),
                                  (2048, 10240), (100, 2816), (3001, 1344)])
 def test_qmv_dma_layouts(N, K, bits, out, monkeypatch):
-    monkeypatch.setenv("BITMM_QMV_PATH", "dma")
+    monkeypatch.setenv("BITMM_QMV_PATH", "auto")
     d = I.random_dense(1, N, K, bits, seed=N + 3 * K + bits)
     got = G.to_f64(G.run_dense("bitmm_qmv", d, out))
     G.assert_close(got, oracle_dense(d), out, f"qmv[dma] N{N} K{K} b{bits}")
