@@ -77,6 +77,18 @@ __device__ __forceinline__ float wave_sum_lane63(float v) {
   return v;
 }
 
+// v_fma_mix_f32: a * h + c in f32 with one rounding, h the low (HI = 0) or high
+// (HI = 1) f16 half of `packed`, converted exactly.
+template <int HI>
+__device__ __forceinline__ float fma_mix_f16(float a, uint32_t packed, float c) {
+  float d;
+  if constexpr (HI)
+    asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel:[0,1,0] op_sel_hi:[0,1,0]" : "=v"(d) : "v"(a), "v"(packed), "v"(c));
+  else
+    asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel:[0,0,0] op_sel_hi:[0,1,0]" : "=v"(d) : "v"(a), "v"(packed), "v"(c));
+  return d;
+}
+
 // Sum over each aligned group of L lanes (L = 16, 32 or 64), with the same DPP
 // steps: the group's sum ends in its last lane (lane L-1 of the group).
 template <int L>

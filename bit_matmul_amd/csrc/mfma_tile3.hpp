@@ -25,8 +25,9 @@
 // K order within a group (a contraction, so any order that pairs x and w alike is
 // exact): at sub-step t, MFMA lane group j takes 32-bit code word 2j + t of the group
 // (4-bit) or words 4j + 2t, 4j + 2t + 1 (8-bit), and the matching 8 activations,
-// 16-byte chunk 2j + t of the group's activation row. w = fma(s, q, b) in f32,
-// rounded to bf16 for the MFMA.
+// 16-byte chunk 2j + t of the group's activation row. w = s q + b in f32 (one
+// fused multiply-add on an exact f16 form of the code, see read_raw), rounded to
+// bf16 for the MFMA.
 #pragma once
 
 #include "common.hpp"
@@ -150,11 +151,16 @@ struct MmTile3 {
     };
 
     // ---- dequantization of one B operand half, in pieces ----
-    // Raw inputs of half t of group g for column block nb: the code word(s), scale
-    // and bias, read from the weight buffer of the group's step.
+    // Codes as exact f16 values: a code field masked into 0x6400 (1024.0) reads as
+    // 1024 + q when it sits in bits 0..3 (or 0..7 at 8 bits) of a 16-bit half and as
+    // 1024 + 16q in bits 4..7, so w = s q + b is one v_fma_mix_f32 per code:
+    //   s * (1024 + q) + (b - 1024 s)   or   (s / 16) * (1024 + 16 q) + (b - 64 s).
+    // Raw inputs of half t of group g for column block nb: four registers of packed
+    // f16 code values and the affine constants, from the weight buffer of the
+    // group's step.
     struct Raw {
-      uint32_t wd[BITS / 4];  // 4-bit: word 2j + t; 8-bit: words 4j + 2t, 4j + 2t + 1
-      float scale, bias;
+      uint32_t m[4];       // 4-bit: (q0,q4) (q1,q5) (q2,q6) (q3,q7); 8-bit: (q0,q2) (q1,q3) (q4,q6) (q5,q7)
+      float s, b0, s16, b1;
     };
     auto read_raw = [&](int g, int t, int nb, Raw& raw) {
       const int buf = (g / GPS) % 3;
@@ -162,30 +168,63 @@ struct MmTile3 {
       const char* wbuf = wb + buf * WB;
       const uint32_t* sbuf = reinterpret_cast<const uint32_t*>(sb) + buf * 2 * SB;
       const int r = (wn * NBW + nb) * 16 + ln;
-      raw.scale = __uint_as_float(sbuf[r * GPS + gs] << 16);
-      raw.bias = __uint_as_float(sbuf[SB + r * GPS + gs] << 16);
+      const float scale = __uint_as_float(sbuf[r * GPS + gs] << 16);
+      const float bias = __uint_as_float(sbuf[SB + r * GPS + gs] << 16);
+      raw.s = scale;
+      raw.b0 = fmaf(-1024.f, scale, bias);
+      const uint32_t magic = 0x64006400u;  // f16 pair (1024, 1024)
       if constexpr (BITS == 4) {
         // word 2j + t of the group: byte 32 gs + 8 j + 4 t of the row segment
-        raw.wd[0] = *reinterpret_cast<const uint32_t*>(wbuf + loff(r, 2 * gs + (lj >> 1)) + (lj & 1) * 8 + t * 4);
+        const uint32_t wd = *reinterpret_cast<const uint32_t*>(wbuf + loff(r, 2 * gs + (lj >> 1)) + (lj & 1) * 8 + t * 4);
+        const uint32_t w8 = wd >> 8;
+        raw.m[0] = and_or_b32(wd, 0x000F000Fu, magic);
+        raw.m[1] = and_or_b32(wd, 0x00F000F0u, magic);
+        raw.m[2] = and_or_b32(w8, 0x000F000Fu, magic);
+        raw.m[3] = and_or_b32(w8, 0x00F000F0u, magic);
+        raw.s16 = scale * 0.0625f;
+        raw.b1 = fmaf(-64.f, scale, bias);
       } else {
         // words 4j + 2t, 4j + 2t + 1: chunk 4 gs + j, bytes 8 t .. 8 t + 7
         const uint2 v = *reinterpret_cast<const uint2*>(wbuf + loff(r, 4 * gs + lj) + t * 8);
-        raw.wd[0] = v.x;
-        raw.wd[1] = v.y;
+        raw.m[0] = and_or_b32(v.x, 0x00FF00FFu, magic);
+        raw.m[1] = and_or_b32(v.x >> 8, 0x00FF00FFu, magic);
+        raw.m[2] = and_or_b32(v.y, 0x00FF00FFu, magic);
+        raw.m[3] = and_or_b32(v.y >> 8, 0x00FF00FFu, magic);
+        raw.s16 = scale;
+        raw.b1 = raw.b0;
       }
     };
-    // Packed bf16 pair e (k-slots 2e, 2e+1 of the lane's 8) of a B operand.
-    auto pair = [&](const Raw& raw, int e) -> uint32_t {
-      uint32_t c0, c1;
+    // Packed bf16 pair e (k-slots 2e, 2e+1 of the lane's 8, codes 2e and 2e+1 of the
+    // lane's 8 in K order) of a B operand; `m0`, `m1` are the two packed-code
+    // registers it draws on.
+    auto pair = [&](const Raw& raw, int e, uint32_t m0, uint32_t m1) -> uint32_t {
+      float lo, hi;
       if constexpr (BITS == 4) {
-        // slot 2e holds code e of the word's low nibbles, slot 2e+1 the high nibble
-        c0 = (raw.wd[0] >> (8 * e)) & 0xFu;
-        c1 = (raw.wd[0] >> (8 * e + 4)) & 0xFu;
+        // codes 2e', 2e'+1 for e' = e & 1 come from m[2e'] (plain) and m[2e'+1] (x16),
+        // in their low halves for e < 2 and their high halves (codes + 4) otherwise
+        if (e < 2) {
+          lo = fma_mix_f16<0>(raw.s, m0, raw.b0);
+          hi = fma_mix_f16<0>(raw.s16, m1, raw.b1);
+        } else {
+          lo = fma_mix_f16<1>(raw.s, m0, raw.b0);
+          hi = fma_mix_f16<1>(raw.s16, m1, raw.b1);
+        }
       } else {
-        c0 = (raw.wd[e >> 1] >> (16 * (e & 1))) & 0xFFu;
-        c1 = (raw.wd[e >> 1] >> (16 * (e & 1) + 8)) & 0xFFu;
+        // codes 2e, 2e+1: low (e even) or high (e odd) halves of m[2(e>>1)], m[2(e>>1)+1]
+        if ((e & 1) == 0) {
+          lo = fma_mix_f16<0>(raw.s, m0, raw.b0);
+          hi = fma_mix_f16<0>(raw.s, m1, raw.b0);
+        } else {
+          lo = fma_mix_f16<1>(raw.s, m0, raw.b0);
+          hi = fma_mix_f16<1>(raw.s, m1, raw.b0);
+        }
       }
-      return pack_bf16x2(fmaf(raw.scale, (float)c0, raw.bias), fmaf(raw.scale, (float)c1, raw.bias));
+      return pack_bf16x2(lo, hi);
+    };
+    // Which packed-code registers pair e uses.
+    auto pair_regs = [](int e) -> int {  // index of the first register; the second is +1
+      if constexpr (BITS == 4) return 2 * (e & 1);
+      else return 2 * (e >> 1);
     };
 
     f32x4_t acc[MB][NBW];
@@ -200,7 +239,7 @@ struct MmTile3 {
     // fixed by the source: one MFMA per fenced piece, the dequantization spread over
     // the pieces, activation reads several row blocks ahead.
     auto half = [&](const char* xbuf, int t, const bf16x8_t (&bcur)[NBW], int gd, int td,
-                    bf16x8_t (&bnew)[NBW]) {
+                    bf16x8_t (&bnew)[NBW], auto&& extra) {
       constexpr int NM = MB * NBW;   // MFMAs in the half
       constexpr int NP = NBW * 4;    // bf16 pairs to dequantize
       // activation reads run PF row blocks (at least 16 MFMAs) ahead of their use
@@ -222,15 +261,17 @@ struct MmTile3 {
           av[mb + PF] = *reinterpret_cast<const u32x4_t*>(xbuf + loff(xrow0 + (mb + PF) * 16 + ln, 2 * lj + t));
         acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av[mb]), bcur[nb],
                                                               acc[mb][nb], 0, 0, 0);
+        extra(i);  // other work placed in this piece (copies for later iterations)
         // pairs p with first MFMA slot >= 2 (the raw reads have landed by then)
 #pragma unroll
         for (int p = 0; p < NP; ++p) {
           const int slot = NM > 2 ? 2 + p * (NM - 2) / NP : NM - 1;
           if (slot == i) {
             // The empty asm statements keep the pair's arithmetic inside this piece.
-            Raw r = raw[p / 4];
-            asm volatile("" : "+v"(r.wd[(p % 4) * BITS / 16]));
-            d[p / 4][p % 4] = pair(r, p % 4);
+            const Raw& r = raw[p / 4];
+            uint32_t m0 = r.m[pair_regs(p % 4)], m1 = r.m[pair_regs(p % 4) + 1];
+            asm volatile("" : "+v"(m0), "+v"(m1));
+            d[p / 4][p % 4] = pair(r, p % 4, m0, m1);
             asm volatile("" : "+v"(d[p / 4][p % 4]));
           }
         }
@@ -252,7 +293,10 @@ struct MmTile3 {
     for (int nb = 0; nb < NBW; ++nb) {
       Raw raw;
       read_raw(0, 0, nb, raw);
-      b0[nb] = __builtin_bit_cast(bf16x8_t, u32x4_t{pair(raw, 0), pair(raw, 1), pair(raw, 2), pair(raw, 3)});
+      uint32_t d4[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) d4[e] = pair(raw, e, raw.m[pair_regs(e)], raw.m[pair_regs(e) + 1]);
+      b0[nb] = __builtin_bit_cast(bf16x8_t, u32x4_t{d4[0], d4[1], d4[2], d4[3]});
     }
 
 #pragma unroll 1
@@ -262,14 +306,48 @@ struct MmTile3 {
       // Copies for later iterations: x of group s+1 into the other x buffer, part
       // s % GPS of weight step S+2 into the third weight buffer. Neither buffer is
       // read in this iteration.
-      copy_x(gn, (s + 1) & 1);
-      copy_part(min(S + 2, nws - 1), s % GPS, (S + 2) % 3);
+      // Their descriptors are formed here; the copy instructions themselves are
+      // spread over the MFMA pieces of half 0, x first (the in-order wait below
+      // relies on the weight-part copies being the last ones issued).
       static_assert(kPartCopies <= 63, "vmcnt range");
+      const __amdgpu_buffer_rsrc_t rx = make_rsrc(x_rows + (int64_t)gn * kGroup, (int64_t)rows * K * 2 - gn * 128);
+      char* xdst = xb + ((s + 1) & 1) * XB;
+      const int Sp = min(S + 2, nws - 1);
+      const int pp = s % GPS;
+      char* wdst = wb + ((S + 2) % 3) * WB;
+      char* sdst = sb + ((S + 2) % 3) * 2 * SB * 4;
+      const int64_t row0 = (int64_t)n0 + pp * PROWS;
+      const __amdgpu_buffer_rsrc_t rw = make_rsrc(reinterpret_cast<const char*>(w) + row0 * rowbytes + Sp * 128,
+                                                  (N - row0) * rowbytes - Sp * 128);
+      constexpr int NCOPY = XC + WC + SC;
+      constexpr int NM0 = MB * NBW;  // pieces of half 0
+      auto copies = [&](int i) {
+#pragma unroll
+        for (int c = 0; c < NCOPY; ++c) {
+          if (c * NM0 / NCOPY != i) continue;
+          if (c < XC) {
+            const int I = wave + c * WAVES;
+            if (XI % WAVES == 0 || I < XI) dma<16>(rx, xoff[c], xdst + I * 1024);
+          } else if (c < XC + WC) {
+            const int j = wave + (c - XC) * WAVES;
+            if (WI % WAVES == 0 || j < WI) dma<16>(rw, woff[c - XC], wdst + (pp * WI + j) * 1024);
+          } else {
+            const int k = c - XC - WC;
+            const int j = wave + k * WAVES;
+            if (SI % WAVES == 0 || j < SI) {
+              const int which = j / (SI / 2);  // 0 scales, 1 biases (uniform per wave)
+              const __amdgpu_buffer_rsrc_t rs = make_rsrc((which ? bi : sc) + row0 * G + Sp * GPS,
+                                                          ((N - row0) * G - Sp * GPS) * 2);
+              dma<2>(rs, soff[k], sdst + (which * SB + pp * PROWS * GPS + (j % (SI / 2)) * 64) * 4);
+            }
+          }
+        }
+      };
       const char* xbuf = xb + (s & 1) * XB;
       // Half 0 of group s while half 1 of group s is dequantized; then half 1 of
       // group s while half 0 of group s+1 is (its weight step, S or S+1, is complete).
-      half(xbuf, 0, b0, s, 1, b1);
-      half(xbuf, 1, b1, gn, 0, b0);
+      half(xbuf, 0, b0, s, 1, b1, copies);
+      half(xbuf, 1, b1, gn, 0, b0, [](int) {});
       // Wait for this iteration's x copies and everything issued before them; the
       // weight-part copies just issued may stay in flight for one more iteration
       // (they are first read two groups or more later). Loads retire in order.
