@@ -125,13 +125,25 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
 // Direct HBM -> LDS copy through a descriptor: lane L's SIZE bytes at byte offset
 // voff land at dst + 16 L (SIZE 16) or in the low half of the 4-byte slot dst + 4 L
 // (SIZE 2), without passing through registers.
+// `soff` (a wave-uniform scalar offset) is added to the address but takes no part in
+// the range check, so it may only carry offsets that stay inside the checked row.
 template <int SIZE>
-__device__ __forceinline__ void dma(__amdgpu_buffer_rsrc_t r, uint32_t voff, char* dst) {
+__device__ __forceinline__ void dma(__amdgpu_buffer_rsrc_t r, uint32_t voff, char* dst, int soff = 0) {
   static_assert(SIZE == 16 || SIZE == 2, "copy size");
   if constexpr (SIZE == 16)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t*)dst, 16, voff, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t*)dst, 16, voff, soff, 0, 0);
   else
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t*)dst, 2, voff, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t*)dst, 2, voff, soff, 0, 0);
 }
+
+// Workgroup barrier without the memory fence of __syncthreads(). The fence makes the
+// compiler wait for every outstanding load, including HBM -> LDS copies meant to stay
+// in flight across the barrier; callers wait for the copies they need themselves
+// (s_waitcnt vmcnt) and consume every LDS read they issue before arriving here. The
+// "memory" clobber keeps the compiler from moving memory accesses across it.
+__device__ __forceinline__ void barrier_no_fence() { asm volatile("s_barrier" ::: "memory"); }
+
+// Cache-policy operand of a buffer load: non-temporal (data read once).
+constexpr int kNonTemporal = 2;
 
 }  // namespace bitmm

@@ -352,7 +352,7 @@ struct MmTile3 {
       // weight-part copies just issued may stay in flight for one more iteration
       // (they are first read two groups or more later). Loads retire in order.
       asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kPartCopies) : "memory");
-      __syncthreads();
+      barrier_no_fence();
     }
 
     // Epilogue: lane holds rows 4*lj + i of column ln in each 16x16 block.

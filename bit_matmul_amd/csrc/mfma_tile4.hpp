@@ -1,0 +1,372 @@
+// Matrix-core tile with 32x32x16 MFMAs: y[rows, n0 .. n0+BN) = x[rows, :] * dequant(w)^T,
+// one 64-wide quantization group per loop body.
+//
+// Workgroup of WN waves, one per SIMD. Every wave owns all BM = 32*MB activation rows of
+// the tile and 32 weight rows (columns of y), so each weight is dequantized exactly once
+// per tile, and each wave's B operand never leaves its registers.
+//
+// The instruction stream is what limits a one-wave-per-SIMD matrix-core loop on gfx950:
+// an MFMA holds the wave's issue port for part of its run, and each other instruction
+// (vector, scalar, LDS or memory) takes a slot of its own. A 32x32x16 MFMA carries twice
+// the work of a 16x16x32 one for the same issue cost, so the per-MFMA budget for the
+// dequantization, the LDS reads and the copies doubles. The design keeps that stream
+// short:
+//   * Weights go straight from HBM to registers: lane (c, h) of wave wn holds, for group
+//     g, the 16 bytes (4-bit) or 32 bytes (8-bit) of weight row n0 + 32 wn + c that hold
+//     codes 32h .. 32h+31 of the group, plus the group's scale and bias. Loads for group
+//     g+3 are issued while group g is multiplied. No LDS traffic, no barrier.
+//   * Activations are the only operand staged in LDS (three buffers of one group, BM rows
+//     x 128 bytes, copied HBM -> LDS without passing through registers, two groups ahead).
+//     One barrier per group.
+//   * Buffer descriptors are formed once; only scalar offsets move with the group. The
+//     loop body is unrolled three times so every LDS buffer index is a constant.
+//
+// K order within a group (a contraction, so any order that pairs x and w alike is exact):
+// MFMA k-step u (0..3) gives k-slot 8h + i of lane (c, h) code 32h + 8u + i of the group,
+// and the A operand of lane (r, h) the activation with the same index: 16-byte chunk
+// 4h + u of the row's 128-byte group segment.
+//
+// Dequantization, per code: w = s q + b as one v_fma_mix_f32 on an exact f16 form of the
+// code (a code field ORed into 0x6400 = 1024.0 reads as 1024 + q in bits 0..7 of a half,
+// or 1024 + 16 q in bits 4..7), so w = s (1024 + q) + (b - 1024 s) or (s/16)(1024 + 16q)
+// + (b - 64 s); rounded to bf16 for the MFMA; f32 accumulation.
+#pragma once
+
+#include <type_traits>
+
+#include "common.hpp"
+
+namespace bitmm {
+
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+template <int BITS, int MB, int WN>
+struct MmTile4 {
+  static constexpr int WAVES = WN;
+  static constexpr int THREADS = 64 * WAVES;
+  static constexpr int BM = 32 * MB;
+  static constexpr int BN = 32 * WN;
+  static constexpr int XB = BM * 128;            // one activation buffer (one group)
+  static constexpr int LDS_BYTES = 3 * XB;
+  static constexpr int XI = BM / 8;              // 1 KB copies per group
+  static constexpr int XC = XI / WAVES;          // copies per wave per group
+  static constexpr int WV = BITS / 4;            // 16-byte code loads per lane per group
+  static constexpr int GB = 8 * BITS;            // bytes of one group of codes (32 WV)
+  static constexpr int WL = WV + 2;              // weight-side loads per group
+  static constexpr int NP = 4 * MB;              // MFMAs per group
+  static constexpr int PF = 4;                   // activation reads in flight
+  static_assert(BITS == 4 || BITS == 8, "bits");
+  static_assert(XI % WAVES == 0, "every wave issues the same number of copies");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+  static_assert(2 * WL + XC <= 63, "vmcnt range");
+  static_assert(WAVES * BM * 64 <= LDS_BYTES, "epilogue staging fits in the activation buffers");
+
+  // Byte offset of 16-byte chunk c of row r in a 128-byte-row tile: rows in blocks of
+  // 16 (2 KB), row r of a block at (r & 7) * 256 + (r >> 3) * 128, chunk c at
+  // (c ^ (r & 7)) * 16. The reads of one MFMA operand (each 16-lane quarter: 16 rows,
+  // one chunk each) and the writes of row-contiguous copies are free of bank conflicts.
+  __device__ static __forceinline__ int loff(int r, int c) {
+    return (r >> 4) * 2048 + (r & 7) * 256 + ((r >> 3) & 1) * 128 + ((c ^ (r & 7)) << 4);
+  }
+  // Inverse for a copy: lane L of the copy into bytes [1024 I, 1024 I + 1024) carries
+  // chunk dma_chunk(I, L) of row dma_row(I, L).
+  __device__ static __forceinline__ int dma_row(int I, int L) {
+    return (I >> 1) * 16 + ((L >> 3) & 1) * 8 + (I & 1) * 4 + (L >> 4);
+  }
+  __device__ static __forceinline__ int dma_chunk(int I, int L) {
+    return (L & 7) ^ ((I & 1) * 4 + (L >> 4));
+  }
+
+  // Raw weight-side registers of one group: codes, scale and bias (bf16 in the low half).
+  struct Wraw {
+    u32x4_t q[WV];
+    uint32_t s, b;
+  };
+  // Affine constants of one group, see the dequantization note above.
+  struct Aff {
+    float s, b0, s16, b1;
+  };
+
+  __device__ static void run(const uint16_t* __restrict__ x_rows_in, int rows_in,
+                             const uint32_t* __restrict__ w_in, const uint16_t* __restrict__ sc_in,
+                             const uint16_t* __restrict__ bi_in, int n0_in, int N, int K,
+                             void* __restrict__ y_rows, bool out_f32, char* lds) {
+    const uint16_t* x_rows = uniform_ptr(x_rows_in);
+    const uint32_t* w = uniform_ptr(w_in);
+    const uint16_t* sc = uniform_ptr(sc_in);
+    const uint16_t* bi = uniform_ptr(bi_in);
+    const int rows = __builtin_amdgcn_readfirstlane(rows_in);
+    const int n0 = __builtin_amdgcn_readfirstlane(n0_in);
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lc = lane & 31;
+    const int lh = lane >> 5;
+    const int G = K / kGroup;
+    const int rowbytes = K * BITS / 8;
+    const int col0 = n0 + wave * 32;  // first weight row of this wave
+
+    // Descriptors for the whole K loop. Out-of-range rows (activation rows past `rows`,
+    // weight rows past N) sit in the checked per-lane offset and read as zeros; the
+    // group offset, always inside a row, travels in the scalar offset.
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(x_rows, (int64_t)rows * K * 2);
+    const __amdgpu_buffer_rsrc_t rw =
+        make_rsrc(reinterpret_cast<const char*>(w) + (int64_t)col0 * rowbytes, (int64_t)(N - col0) * rowbytes);
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(sc + (int64_t)col0 * G, (int64_t)(N - col0) * G * 2);
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(bi + (int64_t)col0 * G, (int64_t)(N - col0) * G * 2);
+    uint32_t xoff[XC];
+#pragma unroll
+    for (int k = 0; k < XC; ++k) {
+      const int I = wave + k * WAVES;
+      xoff[k] = (uint32_t)(dma_row(I, lane) * K * 2 + dma_chunk(I, lane) * 16);
+    }
+    const uint32_t woff = (uint32_t)(lc * rowbytes + lh * 16 * WV);
+    const uint32_t soff = (uint32_t)(lc * G * 2);
+    // Activation read offsets within a buffer for k-step u (row lc of row block 0).
+    int aoff[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) aoff[u] = loff(lc, 4 * lh + u);
+
+    // Default cache policy: the other row tiles of the same columns read these codes
+    // again shortly after, from L2.
+    auto load_w = [&](int g, Wraw& r) {
+      const int gc = min(g, G - 1);  // past the end: a valid group, never used
+#pragma unroll
+      for (int v = 0; v < WV; ++v)
+        r.q[v] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                                 rw, woff + v * 16, gc * GB, 0));
+      r.s = __builtin_amdgcn_raw_buffer_load_b16(rs, soff, gc * 2, 0);
+      r.b = __builtin_amdgcn_raw_buffer_load_b16(rb, soff, gc * 2, 0);
+    };
+    auto copy_x = [&](int g, char* dst, int k) {
+      const int gc = min(g, G - 1);
+      dma<16>(rx, xoff[k], dst + (wave + k * WAVES) * 1024, gc * 128);
+    };
+    auto affine = [&](const Wraw& r) -> Aff {
+      Aff a;
+      a.s = __uint_as_float(r.s << 16);
+      const float b = __uint_as_float(r.b << 16);
+      a.b0 = fmaf(-1024.f, a.s, b);
+      if constexpr (BITS == 4) {
+        a.s16 = a.s * 0.0625f;
+        a.b1 = fmaf(-64.f, a.s, b);
+      } else {
+        a.s16 = a.s;
+        a.b1 = a.b0;
+      }
+      return a;
+    };
+    // Packed f16 code registers for k-step u: 4-bit (q0,q4) (16q1,16q5) (q2,q6)
+    // (16q3,16q7); 8-bit (q0,q2) (q1,q3) (q4,q6) (q5,q7).
+    auto masks = [&](const Wraw& r, int u, uint32_t (&m)[4]) {
+      const uint32_t magic = 0x64006400u;  // f16 pair (1024, 1024)
+      if constexpr (BITS == 4) {
+        const uint32_t wd = r.q[0][u];
+        const uint32_t w8 = wd >> 8;
+        m[0] = and_or_b32(wd, 0x000F000Fu, magic);
+        m[1] = and_or_b32(wd, 0x00F000F0u, magic);
+        m[2] = and_or_b32(w8, 0x000F000Fu, magic);
+        m[3] = and_or_b32(w8, 0x00F000F0u, magic);
+      } else {
+        const uint32_t lo = r.q[u >> 1][2 * (u & 1)];
+        const uint32_t hi = r.q[u >> 1][2 * (u & 1) + 1];
+        m[0] = and_or_b32(lo, 0x00FF00FFu, magic);
+        m[1] = and_or_b32(lo >> 8, 0x00FF00FFu, magic);
+        m[2] = and_or_b32(hi, 0x00FF00FFu, magic);
+        m[3] = and_or_b32(hi >> 8, 0x00FF00FFu, magic);
+      }
+    };
+    // bf16 pair e (k-slots 2e, 2e+1 of the lane's 8) of a B operand.
+    auto pair = [&](const Aff& a, const uint32_t (&m)[4], int e) -> uint32_t {
+      float lo, hi;
+      if constexpr (BITS == 4) {
+        // (w0,w1) low halves of m0,m1; (w2,w3) low of m2,m3; (w4,w5), (w6,w7) high halves
+        const uint32_t p0 = m[2 * (e & 1)], p1 = m[2 * (e & 1) + 1];
+        if (e < 2) {
+          lo = fma_mix_f16<0>(a.s, p0, a.b0);
+          hi = fma_mix_f16<0>(a.s16, p1, a.b1);
+        } else {
+          lo = fma_mix_f16<1>(a.s, p0, a.b0);
+          hi = fma_mix_f16<1>(a.s16, p1, a.b1);
+        }
+      } else {
+        // (w0,w1) low of m0,m1; (w2,w3) high of m0,m1; (w4,w5), (w6,w7) from m2,m3
+        const uint32_t p0 = m[2 * (e >> 1)], p1 = m[2 * (e >> 1) + 1];
+        if ((e & 1) == 0) {
+          lo = fma_mix_f16<0>(a.s, p0, a.b0);
+          hi = fma_mix_f16<0>(a.s, p1, a.b0);
+        } else {
+          lo = fma_mix_f16<1>(a.s, p0, a.b0);
+          hi = fma_mix_f16<1>(a.s, p1, a.b0);
+        }
+      }
+      return pack_bf16x2(lo, hi);
+    };
+
+    f32x16_t acc[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) acc[mb][j] = 0.f;
+
+    char* const xb = lds;
+
+    // ---- prologue: activations of groups 0 and 1, weights of groups 0, 1, 2 ----
+    Wraw wr0, wr1, wr2;
+#pragma unroll
+    for (int k = 0; k < XC; ++k) copy_x(0, xb, k);
+#pragma unroll
+    for (int k = 0; k < XC; ++k) copy_x(1, xb + XB, k);
+    load_w(0, wr0);
+    load_w(1, wr1);
+    load_w(2, wr2);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    Aff acur = affine(wr0);
+    u32x4_t bcur;
+    {
+      uint32_t m[4];
+      masks(wr0, 0, m);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) bcur[e] = pair(acur, m, e);
+    }
+
+    // One group: MFMAs of group g from LDS buffer X with B operands dequantized one
+    // k-step ahead from `wc` (group g) and `wn` (group g+1, for the next body's step 0).
+    // Issues the activation copies of group g+2 and the weight loads of group g+3
+    // (into `wl`). Ends with the wait for the copies of group g+1 and the barrier.
+    auto body = [&](auto Xc, int g, const Wraw& wc, const Wraw& wn, Wraw& wl) {
+      constexpr int X = decltype(Xc)::value;
+      const char* xbuf = xb + X * XB;
+      char* xdst = xb + ((X + 2) % 3) * XB;
+      int ab[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        ab[u] = aoff[u] + X * XB;
+        asm volatile("" : "+v"(ab[u]));
+      }
+      auto aread = [&](int p) -> u32x4_t {
+        const int u = p / MB, mb = p % MB;
+        return *reinterpret_cast<const u32x4_t*>(xbuf - X * XB + ab[u] + mb * 4096);
+      };
+      u32x4_t av[PF];
+#pragma unroll
+      for (int p = 0; p < PF; ++p) av[p] = aread(p);
+      Aff anext = acur;
+      u32x4_t bnext = bcur;
+      uint32_t m[4];
+      uint32_t d[4];
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int p = 0; p < NP; ++p) {
+        const int u = p / MB, mb = p % MB;
+        acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, av[p % PF]),
+                                                          __builtin_bit_cast(bf16x8_t, bcur), acc[mb], 0, 0, 0);
+        if (p + PF < NP) av[p % PF] = aread(p + PF);
+        // Activation copies of group g+2, spread over steps 0..2.
+#pragma unroll
+        for (int k = 0; k < XC; ++k)
+          if (k * (3 * MB) / XC == p) copy_x(g + 2, xdst, k);
+        // Weight loads of group g+3 once the codes of group g are spent (step 3).
+        if (p == 3 * MB) load_w(g + 3, wl);
+        // Dequantization of the next B operand (step u+1 of group g, or step 0 of group
+        // g+1), spread over the step's MFMAs: masks, then four pairs.
+        {
+          const Wraw& src = u < 3 ? wc : wn;
+          const int un = (u + 1) & 3;
+          // slot of each part within the step (mb index)
+          constexpr int S_AFF = 0, S_MASK = 1;
+          if (u == 3 && mb == S_AFF) {
+            uint32_t s = src.s, b = src.b;
+            asm volatile("" : "+v"(s), "+v"(b));
+            Wraw t;
+            t.s = s;
+            t.b = b;
+            anext = affine(t);
+          }
+          if (mb == (MB > 1 ? S_MASK : 0)) {
+            masks(src, un, m);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) asm volatile("" : "+v"(m[e]));
+          }
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int slot = MB > 2 ? 2 + e * (MB - 2) / 4 : MB - 1;
+            if (mb == slot) {
+              d[e] = pair(u == 3 ? anext : acur, m, e);
+              asm volatile("" : "+v"(d[e]));
+            }
+          }
+          if (mb == MB - 1) bnext = u32x4_t{d[0], d[1], d[2], d[3]};
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (mb == MB - 1) bcur = bnext;
+      }
+      acur = anext;
+      // The copies of group g+1 (issued one body earlier) and everything before them
+      // have landed; this body's copies and the two latest weight loads may still fly.
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * WL + XC) : "memory");
+      barrier_no_fence();
+    };
+
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    int g = 0;
+#pragma unroll 1
+    for (; g + 3 <= G; g += 3) {
+      body(I0{}, g, wr0, wr1, wr0);
+      body(I1{}, g + 1, wr1, wr2, wr1);
+      body(I2{}, g + 2, wr2, wr0, wr2);
+    }
+    if (g < G) body(I0{}, g, wr0, wr1, wr0);
+    if (g + 1 < G) body(I1{}, g + 1, wr1, wr2, wr1);
+    // No copy may still be writing LDS when the workgroup moves on or ends, and no wave
+    // reads the activation buffers any more once all have passed this barrier.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    barrier_no_fence();
+
+    // Epilogue: lane (c, h) holds rows 8 (j/4) + 4 h + j%4 of column c in each 32x32 block.
+    const int col = col0 + lc;
+    const bool packed = !out_f32 && (N % 8) == 0 && (reinterpret_cast<uintptr_t>(y_rows) & 15) == 0 &&
+                        col0 + 32 <= N;  // wave-uniform
+    if (packed) {
+      // bf16 through this wave's LDS region (BM rows x 64 bytes), then 16-byte stores
+      // of 8 columns each: 20 stores per 320 rows instead of 160 two-byte ones. Row r
+      // sits at row slot r ^ ((r >> 2) & 1), so the two 32-lane halves of a write
+      // (rows r and r+4) and the four rows of a 16-lane read hit distinct banks.
+      char* tile = lds + wave * (BM * 64);
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int r = mb * 32 + 8 * (j >> 2) + 4 * lh + (j & 3);
+          *reinterpret_cast<uint16_t*>(tile + (r ^ ((r >> 2) & 1)) * 64 + lc * 2) = f32_to_bf16(acc[mb][j]);
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < BM / 16; ++t) {
+        const int r = 16 * t + (lane >> 2);
+        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(tile + (r ^ ((r >> 2) & 1)) * 64 + (lane & 3) * 16);
+        if (r < rows)
+          *reinterpret_cast<u32x4_t*>(static_cast<char*>(y_rows) + ((int64_t)r * N + col0 + (lane & 3) * 8) * 2) = v;
+      }
+    } else if (col < N) {
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int r = mb * 32 + 8 * (j >> 2) + 4 * lh + (j & 3);
+          if (r < rows) {
+            const int64_t o = (int64_t)r * N + col;
+            if (out_f32)
+              static_cast<float*>(y_rows)[o] = acc[mb][j];
+            else
+              static_cast<uint16_t*>(y_rows)[o] = f32_to_bf16(acc[mb][j]);
+          }
+        }
+      }
+    }
+  }
+};
+
+}  // namespace bitmm

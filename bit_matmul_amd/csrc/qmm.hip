@@ -3,6 +3,7 @@
 // tile itself lives in mfma_tile3.hpp.
 #include "kernels.hpp"
 #include "mfma_tile3.hpp"
+#include "mfma_tile4.hpp"
 
 namespace bitmm {
 namespace {
@@ -71,6 +72,20 @@ hipError_t launch_tile3(QmmParams p, hipStream_t stream) {
   return launch_tiles<MmTile3<BITS, 20, 2, 1, 4>>(p, stream);
 }
 
+// 32x32x16 tile: one row of 4 waves, each with 32 weight rows and all the tile's rows
+// (blocks of 32, at most 320 rows: three activation buffers fit in LDS).
+template <int BITS>
+hipError_t launch_tile4(QmmParams p, hipStream_t stream) {
+  const int64_t blocks = (p.M + 31) / 32;
+  const int64_t tiles = (blocks + 9) / 10;
+  const int64_t per = (blocks + tiles - 1) / tiles;
+  if (per <= 2) return launch_tiles<MmTile4<BITS, 2, 4>>(p, stream);
+  if (per <= 4) return launch_tiles<MmTile4<BITS, 4, 4>>(p, stream);
+  if (per <= 6) return launch_tiles<MmTile4<BITS, 6, 4>>(p, stream);
+  if (per <= 8) return launch_tiles<MmTile4<BITS, 8, 4>>(p, stream);
+  return launch_tiles<MmTile4<BITS, 10, 4>>(p, stream);
+}
+
 }  // namespace
 
 hipError_t launch_qmm_mfma(const uint16_t* x, const uint32_t* w, const uint16_t* scales,
@@ -87,6 +102,7 @@ hipError_t launch_qmm_mfma(const uint16_t* x, const uint32_t* w, const uint16_t*
   p.K = (int)K;
   p.out_f32 = out_f32 ? 1 : 0;
   p.tiles_m = p.tiles_n = 0;
+  if (M > 64) return bits == 4 ? launch_tile4<4>(p, stream) : launch_tile4<8>(p, stream);
   return bits == 4 ? launch_tile3<4>(p, stream) : launch_tile3<8>(p, stream);
 }
 

@@ -57,9 +57,6 @@ struct Cfg {
   static constexpr int LDS_BYTES = X_BYTES + XCH * 4;  // + per-chunk activation sums
 };
 
-// Cache-policy operand of a buffer load: non-temporal (the codes are read once).
-constexpr int kNonTemporal = 2;
-
 // Byte offset outside every descriptor: such a load reads zeros.
 constexpr uint32_t kNoChunk = 0x80000000u;
 

@@ -91,7 +91,11 @@ def test_qmm_small_m(M, N, K, bits, out):
 
 
 MFMA_SHAPES = [(8, 16, 64), (9, 100, 192), (16, 128, 128), (33, 70, 320), (130, 300, 576),
-               (129, 257, 1024), (257, 129, 192), (200, 513, 448)]
+               (129, 257, 1024), (257, 129, 192), (200, 513, 448),
+               # row tiles of 32-row blocks: one group, two, three (one unrolled pass),
+               # four; a full 320-row tile, a ragged one, three row tiles
+               (96, 40, 64), (300, 200, 128), (65, 1000, 704), (320, 128, 192),
+               (321, 131, 256), (641, 96, 320)]
 
 
 @pytest.mark.parametrize("bits", [4, 8])
@@ -310,7 +314,9 @@ def test_side_stream_matches_default():
 
 def test_cross_op_consistency():
     """qmm at M=1 is the GEMV; the first rows of an M=600 GEMM agree with M=3;
-    a single-expert gather agrees with qmm."""
+    a single-expert gather agrees with qmm. The gather and the dense GEMM may use
+    different matrix-core tiles (the same bf16 weights, another f32 summation order),
+    so that last pair is held to f32 rounding, not bit equality."""
     t = G.torch()
     d1 = I.random_dense(1, 500, 1024, 4, seed=13)
     assert t.equal(G.run_dense("bitmm_qmv", d1), G.run_dense("bitmm_qmm", d1))
@@ -323,4 +329,4 @@ def test_cross_op_consistency():
     dg = I.Dense("e0", g.x, g.w[0], g.scales[0], g.biases[0], 8)
     yg, _ = G.run_gather(g, "f32")
     ym = G.run_dense("bitmm_qmm", dg, "f32")
-    assert t.equal(yg, ym)
+    G.assert_close(G.to_f64(yg), G.to_f64(ym), "f32", "one-expert gather vs qmm")
