@@ -13,7 +13,7 @@
 //      rows, so each expert's codes are streamed once per column block however many
 //      rows the expert has. Experts without rows exit at once.
 #include "kernels.hpp"
-#include "mfma_tile3.hpp"
+#include "mfma_tile4.hpp"
 
 namespace bitmm {
 namespace {
@@ -111,10 +111,10 @@ __global__ __launch_bounds__(T::THREADS) void gather_qmm_kernel(GatherParams p) 
   const uint16_t* se = p.s + (int64_t)e * p.N * groups;
   const uint16_t* be = p.b + (int64_t)e * p.N * groups;
   for (int r0 = r_begin; r0 < r_end; r0 += T::BM) {
+    if (r0 > r_begin) __syncthreads();  // LDS is reused by the next row block
     const int rows = min(T::BM, r_end - r0);
     T::run(p.x + (int64_t)r0 * p.K, rows, we, se, be, n0, p.N, p.K,
            static_cast<char*>(p.y) + (size_t)r0 * p.N * ysz, p.out_f32 != 0, lds);
-    __syncthreads();  // LDS is reused by the next row block
   }
 }
 
@@ -126,17 +126,32 @@ hipError_t launch_grouped(GatherParams p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Pipelined tile, one row of 4 waves (each expert's weights dequantized once per
-// row block). Row blocks of 16 per tile from the mean rows per expert, with slack for
-// the spread of the routing: experts with more rows loop over row tiles.
+// Scales and biases staged in LDS once per workgroup when the wave's block fits (G <= 48),
+// with 4-byte copies when G is even and both arrays 4-byte aligned.
+template <int BITS, int MB>
+hipError_t launch_sb(GatherParams p, hipStream_t stream) {
+  const int G = p.K / kGroup;
+  const bool wide = G % 2 == 0 && (reinterpret_cast<uintptr_t>(p.s) & 3) == 0 &&
+                    (reinterpret_cast<uintptr_t>(p.b) & 3) == 0;
+  if (G <= 12)
+    return wide ? launch_grouped<BITS, MmTile4<BITS, MB, 4, 3, 2, 1, 12>>(p, stream)
+                : launch_grouped<BITS, MmTile4<BITS, MB, 4, 3, 2, 2, 12>>(p, stream);
+  if (G <= 48)
+    return wide ? launch_grouped<BITS, MmTile4<BITS, MB, 4, 3, 2, 1, 48>>(p, stream)
+                : launch_grouped<BITS, MmTile4<BITS, MB, 4, 3, 2, 2, 48>>(p, stream);
+  return launch_grouped<BITS, MmTile4<BITS, MB, 4>>(p, stream);
+}
+
+// One row of 4 waves, each with 32 weight rows: every expert's weights are dequantized
+// once per column block. Row blocks of 32 per tile from the mean rows per expert, with
+// slack for the spread of the routing; experts with more rows loop over row tiles.
 template <int BITS>
-hipError_t launch_tile3(GatherParams p, hipStream_t stream) {
+hipError_t launch_tile4(GatherParams p, hipStream_t stream) {
   const int64_t mean = p.E > 0 ? (p.B + p.E - 1) / p.E : p.B;
-  const int64_t blocks = (mean + mean / 4 + 15) / 16;
-  if (blocks <= 1) return launch_grouped<BITS, MmTile3<BITS, 1, 2, 1, 4>>(p, stream);
-  if (blocks <= 2) return launch_grouped<BITS, MmTile3<BITS, 2, 2, 1, 4>>(p, stream);
-  if (blocks <= 3) return launch_grouped<BITS, MmTile3<BITS, 3, 2, 1, 4>>(p, stream);
-  return launch_grouped<BITS, MmTile3<BITS, 4, 2, 1, 4>>(p, stream);
+  const int64_t blocks = (mean + mean / 4 + 31) / 32;
+  if (blocks <= 1) return launch_sb<BITS, 1>(p, stream);
+  if (blocks <= 2) return launch_sb<BITS, 2>(p, stream);
+  return launch_sb<BITS, 4>(p, stream);
 }
 
 }  // namespace
@@ -168,7 +183,7 @@ hipError_t launch_gather_qmm(const uint16_t* x, const uint32_t* w, const uint16_
   p.E = (int)E;
   p.tiles_n = 0;
   p.out_f32 = out_f32 ? 1 : 0;
-  return bits == 4 ? launch_tile3<4>(p, stream) : launch_tile3<8>(p, stream);
+  return bits == 4 ? launch_tile4<4>(p, stream) : launch_tile4<8>(p, stream);
 }
 
 }  // namespace bitmm

@@ -40,26 +40,53 @@ namespace bitmm {
 
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-template <int BITS, int MB, int WN>
+// f(integral_constant<int, I>) for I = B .. E-1, in order, each a separate instantiation.
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
+// SBM chooses where a wave finds the scales and biases of its 32 weight rows:
+//   0: two 2-byte loads per group and lane, into registers, PD groups ahead;
+//   1: staged once into LDS by 4-byte copies of the wave's contiguous block (the 32 rows
+//      times G groups of each array are one contiguous span), needs G even and 4-byte
+//      aligned scale and bias arrays;
+//   2: the same with 2-byte copies (each value in a 4-byte LDS slot), any alignment.
+// A per-group load touches one cache line per weight row; the staged copies touch one
+// or two per 64 values. GMAX is the largest G the staging area holds (SBM != 0).
+template <int BITS, int MB, int WN, int PD = 3, int XD = 2, int SBM = 0, int GMAX = 0>
 struct MmTile4 {
   static constexpr int WAVES = WN;
   static constexpr int THREADS = 64 * WAVES;
   static constexpr int BM = 32 * MB;
   static constexpr int BN = 32 * WN;
   static constexpr int XB = BM * 128;            // one activation buffer (one group)
-  static constexpr int LDS_BYTES = 3 * XB;
+  static constexpr int NB = XD + 1;              // activation buffers (copies XD groups ahead)
+  static constexpr int SB_EL = SBM == 1 ? 2 : 4;  // LDS bytes per staged value
+  static constexpr int SB_NDMA = SBM == 0 ? 0 : (32 * GMAX * SB_EL + 255) / 256;  // copies per array
+  static constexpr int SB_ARR = SB_NDMA * 256;    // LDS bytes per array and wave
+  static constexpr int SB_BYTES = WN * 2 * SB_ARR;
+  static constexpr int LDS_BYTES = NB * XB + SB_BYTES;
   static constexpr int XI = BM / 8;              // 1 KB copies per group
   static constexpr int XC = XI / WAVES;          // copies per wave per group
   static constexpr int WV = BITS / 4;            // 16-byte code loads per lane per group
   static constexpr int GB = 8 * BITS;            // bytes of one group of codes (32 WV)
-  static constexpr int WL = WV + 2;              // weight-side loads per group
+  static constexpr int WL = WV + (SBM == 0 ? 2 : 0);  // weight-side loads per group
   static constexpr int NP = 4 * MB;              // MFMAs per group
   static constexpr int PF = 4;                   // activation reads in flight
   static_assert(BITS == 4 || BITS == 8, "bits");
+  static_assert(SBM >= 0 && SBM <= 2 && (SBM == 0) == (GMAX == 0), "scale/bias staging");
   static_assert(XI % WAVES == 0, "every wave issues the same number of copies");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
-  static_assert(2 * WL + XC <= 63, "vmcnt range");
-  static_assert(WAVES * BM * 64 <= LDS_BYTES, "epilogue staging fits in the activation buffers");
+  static_assert(PD >= 2 && XD >= 1 && XD <= PD, "prefetch depths");
+  // Loads issued after the copies of group g+1, when body g waits for them: the weight
+  // loads of that body and the copies and weight loads of the XD-1 bodies after it.
+  static constexpr int VM_AFTER_COPY = WL + (XD - 1) * (XC + WL);
+  static_assert(PD * WL + XD * XC <= 63, "vmcnt range");
+  static_assert(WAVES * BM * 64 <= NB * XB, "epilogue staging fits in the activation buffers");
 
   // Byte offset of 16-byte chunk c of row r in a 128-byte-row tile: rows in blocks of
   // 16 (2 KB), row r of a block at (r & 7) * 256 + (r >> 3) * 128, chunk c at
@@ -97,7 +124,12 @@ struct MmTile4 {
     const uint16_t* bi = uniform_ptr(bi_in);
     const int rows = __builtin_amdgcn_readfirstlane(rows_in);
     const int n0 = __builtin_amdgcn_readfirstlane(n0_in);
-    const int lane = threadIdx.x & 63;
+    // The lane index passes through an empty asm statement so that the per-lane offsets
+    // derived from it are computed here: a caller that runs the tile in a loop would
+    // otherwise get them hoisted out of its loop, each holding a register for good.
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lc = lane & 31;
     const int lh = lane >> 5;
@@ -134,8 +166,17 @@ struct MmTile4 {
       for (int v = 0; v < WV; ++v)
         r.q[v] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
                                                  rw, woff + v * 16, gc * GB, 0));
-      r.s = __builtin_amdgcn_raw_buffer_load_b16(rs, soff, gc * 2, 0);
-      r.b = __builtin_amdgcn_raw_buffer_load_b16(rb, soff, gc * 2, 0);
+      if constexpr (SBM == 0) {
+        r.s = __builtin_amdgcn_raw_buffer_load_b16(rs, soff, gc * 2, 0);
+        r.b = __builtin_amdgcn_raw_buffer_load_b16(rb, soff, gc * 2, 0);
+      }
+    };
+    // Staged scales and biases: this wave's region, value of row lc and group g.
+    char* const sbw = lds + NB * XB + wave * 2 * SB_ARR;
+    auto sb_read = [&](int g, uint32_t& sv, uint32_t& bv) {
+      const int o = (lc * G + min(g, G - 1)) * SB_EL;
+      sv = *reinterpret_cast<const uint16_t*>(sbw + o);
+      bv = *reinterpret_cast<const uint16_t*>(sbw + SB_ARR + o);
     };
     auto copy_x = [&](int g, char* dst, int k) {
       const int gc = min(g, G - 1);
@@ -210,43 +251,70 @@ struct MmTile4 {
 
     char* const xb = lds;
 
-    // ---- prologue: activations of groups 0 and 1, weights of groups 0, 1, 2 ----
-    Wraw wr0, wr1, wr2;
+    // ---- prologue: activations of groups 0 .. XD-1, weights of groups 0 .. PD-1 ----
+    Wraw wr[PD];
 #pragma unroll
-    for (int k = 0; k < XC; ++k) copy_x(0, xb, k);
+    for (int i = 0; i < XD; ++i)
 #pragma unroll
-    for (int k = 0; k < XC; ++k) copy_x(1, xb + XB, k);
-    load_w(0, wr0);
-    load_w(1, wr1);
-    load_w(2, wr2);
+      for (int k = 0; k < XC; ++k) copy_x(i, xb + i * XB, k);
+#pragma unroll
+    for (int i = 0; i < PD; ++i) load_w(i, wr[i]);
+    if constexpr (SBM != 0) {
+      // Lane L of copy j carries values 64 j + L (2-byte form) or 128 j + 2 L, +1 (4-byte
+      // form) of the wave's block; rows past N read as zeros.
+      const int ncopy = (32 * G * SB_EL + 255) / 256;
+      for (int j = 0; j < ncopy; ++j) {
+        const uint32_t vo = (uint32_t)((j * 64 + lane) * (SBM == 1 ? 4 : 2));
+        if constexpr (SBM == 1) {
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t*)(sbw + j * 256), 4, vo, 0, 0, 0);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t*)(sbw + SB_ARR + j * 256), 4, vo, 0, 0, 0);
+        } else {
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t*)(sbw + j * 256), 2, vo, 0, 0, 0);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t*)(sbw + SB_ARR + j * 256), 2, vo, 0, 0, 0);
+        }
+      }
+    }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    Aff acur = affine(wr0);
+    if constexpr (SBM != 0) {
+      uint32_t s0, b0;
+      sb_read(0, s0, b0);
+      wr[0].s = s0;
+      wr[0].b = b0;
+    }
+    Aff acur = affine(wr[0]);
     u32x4_t bcur;
     {
       uint32_t m[4];
-      masks(wr0, 0, m);
+      masks(wr[0], 0, m);
 #pragma unroll
       for (int e = 0; e < 4; ++e) bcur[e] = pair(acur, m, e);
     }
 
-    // One group: MFMAs of group g from LDS buffer X with B operands dequantized one
-    // k-step ahead from `wc` (group g) and `wn` (group g+1, for the next body's step 0).
-    // Issues the activation copies of group g+2 and the weight loads of group g+3
-    // (into `wl`). Ends with the wait for the copies of group g+1 and the barrier.
-    auto body = [&](auto Xc, int g, const Wraw& wc, const Wraw& wn, Wraw& wl) {
-      constexpr int X = decltype(Xc)::value;
-      const char* xbuf = xb + X * XB;
-      char* xdst = xb + ((X + 2) % 3) * XB;
+    // One group: MFMAs of group g from LDS buffer g % NB with B operands dequantized one
+    // k-step ahead from ring slot I (group g) and slot I+1 (group g+1, for the next body's
+    // step 0). Issues the activation copies of group g+XD and the weight loads of group
+    // g+PD (into slot I, spent by then). Ends with the wait for the copies of group g+1
+    // and the barrier.
+    auto body = [&](auto Ic, int g) {
+      constexpr int I = decltype(Ic)::value;
+      const Wraw& wc = wr[I];
+      const Wraw& wn = wr[(I + 1) % PD];
+      uint32_t sn = 0, bn = 0;  // staged scale and bias of group g+1
+      if constexpr (SBM != 0) sb_read(g + 1, sn, bn);
+      // Buffer of group g and of group g + XD: scalar byte offsets.
+      const int xsel = __builtin_amdgcn_readfirstlane((g % NB) * XB);
+      const int xdsel = __builtin_amdgcn_readfirstlane(((g + XD) % NB) * XB);
+      char* xdst = xb + xdsel;
       int ab[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        ab[u] = aoff[u] + X * XB;
+        ab[u] = aoff[u] + xsel;
         asm volatile("" : "+v"(ab[u]));
       }
       auto aread = [&](int p) -> u32x4_t {
         const int u = p / MB, mb = p % MB;
-        return *reinterpret_cast<const u32x4_t*>(xbuf - X * XB + ab[u] + mb * 4096);
+        return *reinterpret_cast<const u32x4_t*>(xb + ab[u] + mb * 4096);
       };
       u32x4_t av[PF];
 #pragma unroll
@@ -262,12 +330,12 @@ struct MmTile4 {
         acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, av[p % PF]),
                                                           __builtin_bit_cast(bf16x8_t, bcur), acc[mb], 0, 0, 0);
         if (p + PF < NP) av[p % PF] = aread(p + PF);
-        // Activation copies of group g+2, spread over steps 0..2.
+        // Activation copies of group g+XD, spread over steps 0..2.
 #pragma unroll
         for (int k = 0; k < XC; ++k)
-          if (k * (3 * MB) / XC == p) copy_x(g + 2, xdst, k);
-        // Weight loads of group g+3 once the codes of group g are spent (step 3).
-        if (p == 3 * MB) load_w(g + 3, wl);
+          if (k * (3 * MB) / XC == p) copy_x(g + XD, xdst, k);
+        // Weight loads of group g+PD once the codes of group g are spent (step 3).
+        if (p == 3 * MB) load_w(g + PD, wr[I]);
         // Dequantization of the next B operand (step u+1 of group g, or step 0 of group
         // g+1), spread over the step's MFMAs: masks, then four pairs.
         {
@@ -276,7 +344,7 @@ struct MmTile4 {
           // slot of each part within the step (mb index)
           constexpr int S_AFF = 0, S_MASK = 1;
           if (u == 3 && mb == S_AFF) {
-            uint32_t s = src.s, b = src.b;
+            uint32_t s = SBM == 0 ? src.s : sn, b = SBM == 0 ? src.b : bn;
             asm volatile("" : "+v"(s), "+v"(b));
             Wraw t;
             t.s = s;
@@ -302,31 +370,30 @@ struct MmTile4 {
         if (mb == MB - 1) bcur = bnext;
       }
       acur = anext;
-      // The copies of group g+1 (issued one body earlier) and everything before them
-      // have landed; this body's copies and the two latest weight loads may still fly.
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * WL + XC) : "memory");
+      // The copies of group g+1 (issued XD-1 bodies earlier) and everything before them
+      // have landed; later copies and weight loads may still fly.
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(VM_AFTER_COPY) : "memory");
       barrier_no_fence();
     };
 
-    using I0 = std::integral_constant<int, 0>;
-    using I1 = std::integral_constant<int, 1>;
-    using I2 = std::integral_constant<int, 2>;
+    // The ring slot of group g is g % PD: the loop body covers PD groups so that every
+    // slot index is a constant; the last G % PD groups run one body each.
     int g = 0;
 #pragma unroll 1
-    for (; g + 3 <= G; g += 3) {
-      body(I0{}, g, wr0, wr1, wr0);
-      body(I1{}, g + 1, wr1, wr2, wr1);
-      body(I2{}, g + 2, wr2, wr0, wr2);
-    }
-    if (g < G) body(I0{}, g, wr0, wr1, wr0);
-    if (g + 1 < G) body(I1{}, g + 1, wr1, wr2, wr1);
+    for (; g + PD <= G; g += PD) static_for<0, PD>([&](auto Ic) { body(Ic, g + decltype(Ic)::value); });
+    static_for<0, PD - 1>([&](auto Ic) {
+      if (g + decltype(Ic)::value < G) body(Ic, g + decltype(Ic)::value);
+    });
     // No copy may still be writing LDS when the workgroup moves on or ends, and no wave
     // reads the activation buffers any more once all have passed this barrier.
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     barrier_no_fence();
-
     // Epilogue: lane (c, h) holds rows 8 (j/4) + 4 h + j%4 of column c in each 32x32 block.
-    const int col = col0 + lc;
+    // (Offsets recomputed from an opaque lane index, as at the top.)
+    int etid = threadIdx.x;
+    asm volatile("" : "+v"(etid));
+    const int elane = etid & 63, elc = elane & 31, elh = elane >> 5;
+    const int col = col0 + elc;
     const bool packed = !out_f32 && (N % 8) == 0 && (reinterpret_cast<uintptr_t>(y_rows) & 15) == 0 &&
                         col0 + 32 <= N;  // wave-uniform
     if (packed) {
@@ -339,23 +406,23 @@ struct MmTile4 {
       for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
-          const int r = mb * 32 + 8 * (j >> 2) + 4 * lh + (j & 3);
-          *reinterpret_cast<uint16_t*>(tile + (r ^ ((r >> 2) & 1)) * 64 + lc * 2) = f32_to_bf16(acc[mb][j]);
+          const int r = mb * 32 + 8 * (j >> 2) + 4 * elh + (j & 3);
+          *reinterpret_cast<uint16_t*>(tile + (r ^ ((r >> 2) & 1)) * 64 + elc * 2) = f32_to_bf16(acc[mb][j]);
         }
       }
 #pragma unroll
       for (int t = 0; t < BM / 16; ++t) {
-        const int r = 16 * t + (lane >> 2);
-        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(tile + (r ^ ((r >> 2) & 1)) * 64 + (lane & 3) * 16);
+        const int r = 16 * t + (elane >> 2);
+        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(tile + (r ^ ((r >> 2) & 1)) * 64 + (elane & 3) * 16);
         if (r < rows)
-          *reinterpret_cast<u32x4_t*>(static_cast<char*>(y_rows) + ((int64_t)r * N + col0 + (lane & 3) * 8) * 2) = v;
+          *reinterpret_cast<u32x4_t*>(static_cast<char*>(y_rows) + ((int64_t)r * N + col0 + (elane & 3) * 8) * 2) = v;
       }
     } else if (col < N) {
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
-          const int r = mb * 32 + 8 * (j >> 2) + 4 * lh + (j & 3);
+          const int r = mb * 32 + 8 * (j >> 2) + 4 * elh + (j & 3);
           if (r < rows) {
             const int64_t o = (int64_t)r * N + col;
             if (out_f32)

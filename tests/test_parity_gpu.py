@@ -133,6 +133,31 @@ def test_gather_small(ci, N, K, bits, out):
     assert np.array_equal(w[1:g.E + 2].view(np.int32), exp_off)
 
 
+@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("N,K", [(96, 1856), (70, 3200), (64, 2816), (40, 704), (48, 512)])
+@pytest.mark.parametrize("misaligned", [False, True])
+def test_gather_scale_staging(N, K, bits, misaligned):
+    """Every way the grouped GEMM can fetch scales and biases: staged in LDS by 4-byte
+    copies (G even, arrays 4-byte aligned), by 2-byte copies (G odd, or the arrays only
+    2-byte aligned), and loaded per group (G > 48), on ragged expert segments."""
+    t = G.torch()
+    g = I.random_gather([37, 0, 5, 70, 33], N=N, K=K, bits=bits, seed=N + K + bits)
+    x, w, s, b, e = G.gather_to_dev(g)
+    if misaligned:  # views that start 2 bytes into a fresh allocation
+        def shift(a):
+            buf = t.empty(a.numel() + 1, dtype=a.dtype, device=a.device)
+            v = buf[1:].view(a.shape)
+            v.copy_(a)
+            return v
+        s, b = shift(s), shift(b)
+        assert s.data_ptr() % 4 == 2 and b.data_ptr() % 4 == 2
+    y = t.empty((g.B, g.N), dtype=t.bfloat16, device=G.dev())
+    ws = t.empty(bm.bitmm_gather_qmm_workspace_bytes(g.B, g.N, g.E), dtype=t.uint8, device=G.dev())
+    bm.bitmm_gather_qmm(x, w, s, b, e, y, ws, g.bits)
+    ref = oracle.gather_qmm(g.x, g.w, g.scales, g.biases, g.expert_idx, bits)
+    G.assert_close(G.to_f64(y), ref, "bf16", f"gather staging N{N} K{K} b{bits} mis{misaligned}")
+
+
 # ---------------------------------------------------------------------------
 # Exact cases
 # ---------------------------------------------------------------------------
