@@ -1,8 +1,11 @@
-// Host side of the GEMV / small-M path. Two kernel forms:
+// Host side of the GEMV / small-M path. Three kernel forms:
 //   qmv_dma_kernel (qmv_dma.hpp): one activation row, K up to 5 chunks per lane
 //     (K <= 10240 at 4 bits, <= 5120 at 8 bits), the decode GEMV;
+//   qmv_split_kernel (qmv_split.hpp): up to 8 activation rows with K split across the
+//     waves of a workgroup (K <= 16384 at 4 bits and 8192 at 8 bits for up to 3 rows,
+//     half that from 4 rows), the small-M prefill tail;
 //   qmv_kernel (qmv_impl.hpp): up to 8 activation rows per launch, any K (several
-//     passes over K when a row does not fit), the small-M prefill tail.
+//     passes over K when a row does not fit), for what the other two do not take.
 #include <stdlib.h>
 
 #include <atomic>
@@ -10,6 +13,7 @@
 #include "kernels.hpp"
 #include "qmv_dma.hpp"
 #include "qmv_impl.hpp"
+#include "qmv_split.hpp"
 
 namespace bitmm {
 
@@ -66,6 +70,19 @@ hipError_t launch_qmv(const uint16_t* x, const uint32_t* w, const uint16_t* scal
     const int wpc = env_int("BITMM_QMV_WAVES_PER_CU");
     return bits == 4 ? qmv_dma_detail::launch_bits<4>(dp, compute_units(), wpc, stream)
                      : qmv_dma_detail::launch_bits<8>(dp, compute_units(), wpc, stream);
+  }
+  if (forced_path() == 0 && M <= 8 && qmv_split_detail::fits(K, bits, M)) {
+    qmv_split_detail::Params sp;
+    sp.x = x;
+    sp.w = w;
+    sp.s = scales;
+    sp.b = biases;
+    sp.y = y;
+    sp.N = (int)N;
+    sp.K = (int)K;
+    sp.out_f32 = out_f32 ? 1 : 0;
+    return bits == 4 ? qmv_split_detail::launch_bits<4>(sp, (int)M, stream)
+                     : qmv_split_detail::launch_bits<8>(sp, (int)M, stream);
   }
   for (int64_t m0 = 0; m0 < M; m0 += 8) {
     const int mr = (int)(M - m0 < 8 ? M - m0 : 8);

@@ -38,8 +38,8 @@ def oracle_dense(d):
 # ---------------------------------------------------------------------------
 
 QMV_SHAPES = [(1, 1, 64), (1, 256, 512), (1, 300, 640), (1, 257, 192), (1, 64, 8192 + 64),
-              (2, 77, 320), (3, 133, 5120), (5, 40, 576), (7, 19, 128), (8, 33, 256),
-              (11, 50, 192)]
+              (1, 70, 12288), (2, 77, 320), (3, 133, 5120), (3, 37, 16384), (4, 66, 8192),
+              (5, 40, 576), (6, 45, 8256), (7, 19, 128), (8, 33, 256), (11, 50, 192)]
 
 
 @pytest.mark.parametrize("bits", [4, 8])
