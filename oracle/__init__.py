@@ -63,6 +63,12 @@ class Oracle:
         lib.oracle_gather_qmm_points.argtypes = [P, P, P, P, P, I64, I64, I64, I64, I, I,
                                                  P, P, I64, P, I]
         lib.oracle_gather_qmm_points.restype = I
+        lib.oracle_gather_qmm_indexed.argtypes = [P, P, P, P, P, P, I64, I64, I64, I64, I64, I, I,
+                                                  P, I]
+        lib.oracle_gather_qmm_indexed.restype = I
+        lib.oracle_gather_qmm_indexed_points.argtypes = [P, P, P, P, P, P, I64, I64, I64, I64,
+                                                         I64, I, I, P, P, I64, P, I]
+        lib.oracle_gather_qmm_indexed_points.restype = I
         self.lib = lib
         self.path = path
 
@@ -163,6 +169,46 @@ class Oracle:
                                                  int(threads)))
         return y
 
+    def gather_qmm_indexed(self, x, w, scales, biases, token_idx, expert_idx, bits: int,
+                           group: int = 64, threads: int = 0, rows=None, cols=None) -> np.ndarray:
+        """y[B,N] (float64), or y at the points (rows[i], cols[i]): row r reads x row
+        token_idx[r] (row r when token_idx is None) and expert expert_idx[r]."""
+        x, px = _c(x, np.uint16)
+        w, pw = _c(w, np.uint32)
+        s, ps = _c(scales, np.uint16)
+        b, pb = _c(biases, np.uint16)
+        e, pe = _c(expert_idx, np.int32)
+        T, K = x.shape
+        E, N = w.shape[0], w.shape[1]
+        B = e.shape[0]
+        if token_idx is None:
+            pt = None
+            if T != B:
+                raise ValueError("oracle.gather_qmm_indexed: x rows must equal B without token_idx")
+        else:
+            t, pt = _c(token_idx, np.int32)
+            if t.shape != (B,):
+                raise ValueError("oracle.gather_qmm_indexed: token_idx shape")
+        if (w.shape != (E, N, K * bits // 32) or s.shape != (E, N, K // group)
+                or b.shape != s.shape or e.ndim != 1):
+            raise ValueError("oracle.gather_qmm_indexed: inconsistent shapes")
+        if rows is None:
+            y = np.empty((B, N), dtype=np.float64)
+            _check(self.lib.oracle_gather_qmm_indexed(px, pw, ps, pb, pt, pe, B, N, K, E, T, bits,
+                                                      group, y.ctypes.data_as(ctypes.c_void_p),
+                                                      int(threads)))
+            return y
+        r, pr = _c(rows, np.int64)
+        c, pc = _c(cols, np.int64)
+        if r.shape != c.shape:
+            raise ValueError("oracle.gather_qmm_indexed: rows and cols differ in shape")
+        y = np.empty(r.shape, dtype=np.float64)
+        _check(self.lib.oracle_gather_qmm_indexed_points(px, pw, ps, pb, pt, pe, B, N, K, E, T,
+                                                         bits, group, pr, pc, r.size,
+                                                         y.ctypes.data_as(ctypes.c_void_p),
+                                                         int(threads)))
+        return y
+
 
 def _c(a, dtype):
     a = np.ascontiguousarray(a, dtype=dtype)
@@ -218,6 +264,12 @@ def qmm_points(x, w, scales, biases, rows, cols, bits, group=64, threads=0):
 
 def gather_qmm(x, w, scales, biases, expert_idx, bits, group=64, threads=0):
     return get().gather_qmm(x, w, scales, biases, expert_idx, bits, group, threads)
+
+
+def gather_qmm_indexed(x, w, scales, biases, token_idx, expert_idx, bits, group=64, threads=0,
+                       rows=None, cols=None):
+    return get().gather_qmm_indexed(x, w, scales, biases, token_idx, expert_idx, bits, group,
+                                    threads, rows, cols)
 
 
 def gather_qmm_points(x, w, scales, biases, expert_idx, rows, cols, bits, group=64, threads=0):

@@ -29,6 +29,13 @@
  *     stop accumulating in bf16); the oracle uses f64, the exact definition.
  * A row whose expert id lies outside [0, E) contributes a zero row.
  *
+ * The indexed form is the general GatherQMM the pages name (PR #1562: the MoE
+ * layer's quantized GatherQMM; epic #1536 and issue #1538: the decode-time expert
+ * kernels that run the same product one token at a time): row r of the output
+ * reads activation row token_idx[r] of x[T, K] (row r itself when no token index
+ * is given) and the weights of expert expert_idx[r], in any order. A row whose
+ * token or expert id is out of range is a zero row.
+ *
  * Each output is summed sequentially in k order, and threads only split the
  * set of outputs, so results are bitwise identical for any thread count.
  *
@@ -117,7 +124,8 @@ typedef struct {
   const uint16_t* s;
   const uint16_t* b;
   const int32_t* expert_idx; /* NULL for the dense case */
-  int64_t N, K, E;
+  const int32_t* token_idx;  /* NULL: output row r reads activation row r */
+  int64_t N, K, E, T;
   int bits, group;
   /* outputs: either all rows x cols, or a list of points */
   int64_t rows;
@@ -135,10 +143,15 @@ static double eval_point(const problem_t* p, int64_t r, int64_t n) {
     e = p->expert_idx[r];
     if (e < 0 || e >= p->E) return 0.0;
   }
+  int64_t t = r;
+  if (p->token_idx) {
+    t = p->token_idx[r];
+    if (t < 0 || t >= p->T) return 0.0;
+  }
   const uint32_t* w_row = p->w + (e * p->N + n) * words;
   const uint16_t* s_row = p->s + (e * p->N + n) * groups;
   const uint16_t* b_row = p->b + (e * p->N + n) * groups;
-  return dot_row(p->x + r * p->K, w_row, s_row, b_row, p->K, p->bits, p->group);
+  return dot_row(p->x + t * p->K, w_row, s_row, b_row, p->K, p->bits, p->group);
 }
 
 typedef struct {
@@ -211,7 +224,7 @@ int oracle_qmm(const uint16_t* x, const uint32_t* w, const uint16_t* scales,
                const uint16_t* biases, int64_t M, int64_t N, int64_t K, int bits, int group,
                double* y, int nthreads) {
   if (M < 0 || check_args(N, K, bits, group)) return -1;
-  problem_t p = {x, w, scales, biases, NULL, N, K, 1, bits, group, M, NULL, NULL, M * N, y};
+  problem_t p = {x, w, scales, biases, NULL, NULL, N, K, 1, M, bits, group, M, NULL, NULL, M * N, y};
   return run(&p, nthreads);
 }
 
@@ -222,7 +235,7 @@ int oracle_qmm_points(const uint16_t* x, const uint32_t* w, const uint16_t* scal
   if (M < 0 || count < 0 || check_args(N, K, bits, group)) return -1;
   for (int64_t i = 0; i < count; ++i)
     if (rows[i] < 0 || rows[i] >= M || cols[i] < 0 || cols[i] >= N) return -2;
-  problem_t p = {x, w, scales, biases, NULL, N, K, 1, bits, group, M, rows, cols, count, y};
+  problem_t p = {x, w, scales, biases, NULL, NULL, N, K, 1, M, bits, group, M, rows, cols, count, y};
   return run(&p, nthreads);
 }
 
@@ -230,7 +243,7 @@ int oracle_gather_qmm(const uint16_t* x, const uint32_t* w, const uint16_t* scal
                       const uint16_t* biases, const int32_t* expert_idx, int64_t B, int64_t N,
                       int64_t K, int64_t E, int bits, int group, double* y, int nthreads) {
   if (B < 0 || E < 1 || check_args(N, K, bits, group)) return -1;
-  problem_t p = {x, w, scales, biases, expert_idx, N, K, E, bits, group, B, NULL, NULL, B * N, y};
+  problem_t p = {x, w, scales, biases, expert_idx, NULL, N, K, E, B, bits, group, B, NULL, NULL, B * N, y};
   return run(&p, nthreads);
 }
 
@@ -242,7 +255,28 @@ int oracle_gather_qmm_points(const uint16_t* x, const uint32_t* w, const uint16_
   if (B < 0 || E < 1 || count < 0 || check_args(N, K, bits, group)) return -1;
   for (int64_t i = 0; i < count; ++i)
     if (rows[i] < 0 || rows[i] >= B || cols[i] < 0 || cols[i] >= N) return -2;
-  problem_t p = {x, w, scales, biases, expert_idx, N, K, E, bits, group, B, rows, cols, count, y};
+  problem_t p = {x, w, scales, biases, expert_idx, NULL, N, K, E, B, bits, group, B, rows, cols, count, y};
+  return run(&p, nthreads);
+}
+
+int oracle_gather_qmm_indexed(const uint16_t* x, const uint32_t* w, const uint16_t* scales,
+                              const uint16_t* biases, const int32_t* token_idx,
+                              const int32_t* expert_idx, int64_t B, int64_t N, int64_t K,
+                              int64_t E, int64_t T, int bits, int group, double* y, int nthreads) {
+  if (B < 0 || E < 1 || T < 0 || check_args(N, K, bits, group)) return -1;
+  problem_t p = {x, w, scales, biases, expert_idx, token_idx, N, K, E, T, bits, group, B, NULL, NULL, B * N, y};
+  return run(&p, nthreads);
+}
+
+int oracle_gather_qmm_indexed_points(const uint16_t* x, const uint32_t* w, const uint16_t* scales,
+                                     const uint16_t* biases, const int32_t* token_idx,
+                                     const int32_t* expert_idx, int64_t B, int64_t N, int64_t K,
+                                     int64_t E, int64_t T, int bits, int group, const int64_t* rows,
+                                     const int64_t* cols, int64_t count, double* y, int nthreads) {
+  if (B < 0 || E < 1 || T < 0 || count < 0 || check_args(N, K, bits, group)) return -1;
+  for (int64_t i = 0; i < count; ++i)
+    if (rows[i] < 0 || rows[i] >= B || cols[i] < 0 || cols[i] >= N) return -2;
+  problem_t p = {x, w, scales, biases, expert_idx, token_idx, N, K, E, T, bits, group, B, rows, cols, count, y};
   return run(&p, nthreads);
 }
 

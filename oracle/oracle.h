@@ -47,6 +47,19 @@ int oracle_gather_qmm_points(const uint16_t* x, const uint32_t* w, const uint16_
                              const int64_t* rows, const int64_t* cols, int64_t count, double* y,
                              int nthreads);
 
+/* y[B*N]: row r reads x row token_idx[r] of x[T, K] (row r when token_idx is NULL)
+   and expert expert_idx[r] of w; any order; zero row if either id is out of range */
+int oracle_gather_qmm_indexed(const uint16_t* x, const uint32_t* w, const uint16_t* scales,
+                              const uint16_t* biases, const int32_t* token_idx,
+                              const int32_t* expert_idx, int64_t B, int64_t N, int64_t K,
+                              int64_t E, int64_t T, int bits, int group, double* y, int nthreads);
+
+int oracle_gather_qmm_indexed_points(const uint16_t* x, const uint32_t* w, const uint16_t* scales,
+                                     const uint16_t* biases, const int32_t* token_idx,
+                                     const int32_t* expert_idx, int64_t B, int64_t N, int64_t K,
+                                     int64_t E, int64_t T, int bits, int group, const int64_t* rows,
+                                     const int64_t* cols, int64_t count, double* y, int nthreads);
+
 #ifdef __cplusplus
 }
 #endif

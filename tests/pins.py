@@ -310,6 +310,67 @@ def check_points_and_threads(O):
         O.gather_qmm_points(g.x, g.w, g.scales, g.biases, g.expert_idx, r, c, 8), gy[r, c])
 
 
+def _indexed_problem(T, B, E, N, K, bits, seed):
+    """Random tokens and experts per output row, unsorted, with repeats."""
+    rng = np.random.default_rng(seed)
+    x = I.to_bf16_bits(rng.standard_normal((T, K)))
+    w = I.random_words(rng, (E, N, K * bits // 32))
+    s = I.random_scales(rng, (E, N, K // 64))
+    b = I.to_bf16_bits(rng.uniform(-0.2, 0.2, size=(E, N, K // 64)))
+    tok = rng.integers(0, T, B).astype(np.int32)
+    exp = rng.integers(0, E, B).astype(np.int32)
+    return x, w, s, b, tok, exp
+
+
+def check_indexed_brute_force(O):
+    """The indexed gather (row r reads x[token_idx[r]] and expert expert_idx[r], any
+    order) against numpy: rows gathered by fancy indexing, each expert dequantized
+    densely with the byte-view unpacker, float64 matmul."""
+    for bits in (4, 8):
+        for T, B, E, N, K in ((1, 8, 16, 9, 128), (3, 7, 5, 17, 192), (6, 20, 4, 3, 64)):
+            x, w, s, b, tok, exp = _indexed_problem(T, B, E, N, K, bits, seed=T * 100 + B + bits)
+            got = O.gather_qmm_indexed(x, w, s, b, tok, exp, bits)
+            xf = I.bf16_bits_to_f64(x)
+            ref = np.empty((B, N))
+            for r in range(B):
+                W = numpy_dequant(w[exp[r]], s[exp[r]], b[exp[r]], bits)
+                ref[r] = W @ xf[tok[r]]
+            assert np.allclose(got, ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max()), (bits, T, B)
+            # without a token index, row r reads activation row r
+            xr = x[tok]
+            assert np.array_equal(O.gather_qmm_indexed(xr, w, s, b, None, exp, bits), got)
+
+
+def check_indexed_constant(O):
+    """q = 0, b[e] = e + 1, x[t,:] = (t mod 7) + 1, tokens and experts unsorted:
+    y[r,n] = K (e_r + 1)((tok_r mod 7) + 1) exactly; a mis-gathered token or expert
+    gives a wrong integer. Out-of-range ids give zero rows."""
+    T, E, N, K = 9, 6, 5, 128
+    tok = np.array([3, 0, 8, 8, 1, 5, 2, 7, 4, 6, 0, 9, -1, 2], dtype=np.int32)
+    exp = np.array([5, 0, 2, 2, 4, 1, 3, 0, 5, 1, 4, 1, 2, 6], dtype=np.int32)
+    for bits in (4, 8):
+        w = np.zeros((E, N, K * bits // 32), dtype=np.uint32)
+        s = I.to_bf16_bits(np.full((E, N, K // 64), 0.5))
+        b = I.to_bf16_bits(np.broadcast_to((np.arange(E) + 1.0)[:, None, None], (E, N, K // 64)))
+        xv = (np.arange(T) % 7 + 1).astype(np.float64)
+        x = I.to_bf16_bits(np.broadcast_to(xv[:, None], (T, K)))
+        got = O.gather_qmm_indexed(x, w, s, b, tok, exp, bits)
+        ok = (tok >= 0) & (tok < T) & (exp >= 0) & (exp < E)
+        want = np.where(ok[:, None], K * (exp[:, None] + 1.0) * xv[np.clip(tok, 0, T - 1)][:, None], 0.0)
+        assert np.array_equal(got, want * np.ones((1, N))), bits
+        assert np.array_equal(got[~ok], np.zeros((int((~ok).sum()), N)))
+
+
+def check_indexed_points(O):
+    """Point evaluation of the indexed gather equals its full result."""
+    x, w, s, b, tok, exp = _indexed_problem(4, 12, 3, 10, 128, 4, seed=5)
+    full = O.gather_qmm_indexed(x, w, s, b, tok, exp, 4, threads=2)
+    rng = np.random.default_rng(3)
+    r = rng.integers(0, 12, 40)
+    c = rng.integers(0, 10, 40)
+    assert np.array_equal(O.gather_qmm_indexed(x, w, s, b, tok, exp, 4, rows=r, cols=c), full[r, c])
+
+
 ALL_CHECKS = [
     check_bf16_golden,
     check_bf16_vs_torch,
@@ -325,4 +386,7 @@ ALL_CHECKS = [
     check_gather_consistency,
     check_repack_8bit,
     check_points_and_threads,
+    check_indexed_brute_force,
+    check_indexed_constant,
+    check_indexed_points,
 ]

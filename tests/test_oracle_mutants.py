@@ -30,7 +30,7 @@ MUTANTS = {
     "group_of_128": ("int64_t g = k / group;", "int64_t g = k / (2 * group);"),
     "first_k_dropped": ("for (int64_t k = 0; k < K; ++k)", "for (int64_t k = 1; k < K; ++k)"),
     "sign_flipped": ("    acc += oracle_bf16_to_f64(x_row[k])", "    acc -= oracle_bf16_to_f64(x_row[k])"),
-    "x_row_zero_only": ("p->x + r * p->K", "p->x + (r % 1) * p->K"),
+    "x_row_zero_only": ("p->x + t * p->K", "p->x + (t % 1) * p->K"),
     "expert_ignored": ("const uint32_t* w_row = p->w + (e * p->N + n) * words;",
                        "const uint32_t* w_row = p->w + (n) * words;"),
     "expert_scales_ignored": ("const uint16_t* s_row = p->s + (e * p->N + n) * groups;",
@@ -41,6 +41,8 @@ MUTANTS = {
                           "      r = i % p->rows;\n      n = i / p->rows;"),
     "bf16_truncates": ("double r = nearbyint(ldexp(a, 8 - e));", "double r = floor(ldexp(a, 8 - e));"),
     "bf16_ties_away": ("double r = nearbyint(ldexp(a, 8 - e));", "double r = round(ldexp(a, 8 - e));"),
+    "token_ignored": ("return dot_row(p->x + t * p->K,", "return dot_row(p->x + r * p->K,"),
+    "invalid_token_kept": ("if (t < 0 || t >= p->T) return 0.0;", "if (t < 0 || t >= p->T) t = 0;"),
     "bf16_no_overflow": ("if (biased >= 255) return (uint16_t)(sign | 0x7F80u);",
                          "if (biased >= 256) return (uint16_t)(sign | 0x7F80u);"),
 }
