@@ -41,7 +41,8 @@ GROUP = 64
 
 __all__ = [
     "BitmmError", "lib", "bitmm_abi_version", "bitmm_status_string", "bitmm_qmv", "bitmm_qmm",
-    "bitmm_gather_qmm_workspace_bytes", "bitmm_gather_qmm", "qmv", "qmm", "gather_qmm",
+    "bitmm_gather_qmm_workspace_bytes", "bitmm_gather_qmm", "bitmm_gather_qmv", "qmv", "qmm",
+    "gather_qmm", "gather_qmv",
 ]
 
 
@@ -81,6 +82,8 @@ def lib() -> ctypes.CDLL:
         L.bitmm_gather_qmm_workspace_bytes.restype = SZ
         L.bitmm_gather_qmm.argtypes = [P, P, P, P, P, P, I64, I64, I64, I64, I, I, I, P, SZ, P]
         L.bitmm_gather_qmm.restype = I
+        L.bitmm_gather_qmv.argtypes = [P, P, P, P, P, P, P, I64, I64, I64, I64, I64, I, I, I, P]
+        L.bitmm_gather_qmv.restype = I
         _lib = L
     return _lib
 
@@ -197,6 +200,33 @@ def bitmm_gather_qmm(x, w, scales, biases, expert_idx, y, workspace, bits: int,
     return y
 
 
+def bitmm_gather_qmv(x, w, scales, biases, token_idx, expert_idx, y, bits: int,
+                     group_size: int = GROUP, stream=None):
+    """y[r, :] = x[token_idx[r], :] * dequant(w[expert_idx[r]])^T (MoE decode); token_idx
+    may be None (row r reads x[r]); any order; out-of-range ids give zero rows."""
+    torch = _torch()
+    T, K = x.shape
+    E, N = w.shape[0], w.shape[1]
+    B = expert_idx.shape[0]
+    dev = x.device
+    _expect(x, "x", torch.bfloat16, (T, K), dev)
+    if K % group_size:
+        raise ValueError(f"K={K} is not a multiple of group_size={group_size}")
+    _expect(w, "w", torch.int32, (E, N, K * bits // 32), dev)
+    _expect(scales, "scales", torch.bfloat16, (E, N, K // group_size), dev)
+    _expect(biases, "biases", torch.bfloat16, (E, N, K // group_size), dev)
+    _expect(expert_idx, "expert_idx", torch.int32, (B,), dev)
+    if token_idx is not None:
+        _expect(token_idx, "token_idx", torch.int32, (B,), dev)
+    _expect(y, "y", y.dtype, (B, N), dev)
+    st = lib().bitmm_gather_qmv(_ptr(x), _ptr(w), _ptr(scales), _ptr(biases), _ptr(token_idx),
+                                _ptr(expert_idx), _ptr(y), B, N, K, E, T, int(bits),
+                                int(group_size), _out_code(y), _stream_ptr(stream, dev))
+    if st != BITMM_OK:
+        raise BitmmError(st, "bitmm_gather_qmv")
+    return y
+
+
 # ---------------------------------------------------------------------------
 # Allocating conveniences (torch allocates the output; the kernels do the work)
 # ---------------------------------------------------------------------------
@@ -224,3 +254,11 @@ def gather_qmm(x, w, scales, biases, expert_idx, bits: int, out_dtype=None, work
                                 dtype=torch.uint8, device=x.device)
     bitmm_gather_qmm(x, w, scales, biases, expert_idx, y, workspace, bits, stream=stream)
     return y, workspace
+
+
+def gather_qmv(x, w, scales, biases, token_idx, expert_idx, bits: int, out_dtype=None,
+               stream=None):
+    torch = _torch()
+    y = torch.empty((expert_idx.shape[0], w.shape[1]), dtype=out_dtype or torch.bfloat16,
+                    device=x.device)
+    return bitmm_gather_qmv(x, w, scales, biases, token_idx, expert_idx, y, bits, stream=stream)

@@ -146,4 +146,47 @@ __device__ __forceinline__ void barrier_no_fence() { asm volatile("s_barrier" ::
 // Cache-policy operand of a buffer load: non-temporal (data read once).
 constexpr int kNonTemporal = 2;
 
+// Row indirection of the gathered GEMV: output row r = row0 + blockIdx.y reads
+// activation row tok[r] (row r when tok is null) and the weights, scales and biases of
+// expert exp[r]. Dense calls pass exp == nullptr and one row of blocks.
+struct GemvBatch {
+  const int32_t* tok;
+  const int32_t* exp;
+  int T, E;            // activation rows, experts
+  int rows, row0;      // output rows of this launch (gridDim.y) and the first of them
+  int64_t w_stride;    // uint32 words per expert
+  int64_t sb_stride;   // scale (and bias) values per expert
+};
+
+// Moves the operand pointers to the workgroup's output row. Returns false when the
+// row's token or expert id is out of range: the caller then writes zeros to its outputs.
+__device__ __forceinline__ bool gemv_row(const GemvBatch& bt, int K, int N, bool out_f32,
+                                         const uint16_t*& x, const uint32_t*& w, const uint16_t*& s,
+                                         const uint16_t*& b, void*& y) {
+  if (bt.exp == nullptr) return true;
+  const int r = bt.row0 + (int)blockIdx.y;
+  const int e = bt.exp[r];
+  const int t = bt.tok ? bt.tok[r] : r;
+  y = static_cast<char*>(y) + (size_t)r * N * (out_f32 ? 4 : 2);
+  if (e < 0 || e >= bt.E || t < 0 || t >= bt.T) return false;
+  x += (int64_t)t * K;
+  w += (int64_t)e * bt.w_stride;
+  s += (int64_t)e * bt.sb_stride;
+  b += (int64_t)e * bt.sb_stride;
+  return true;
+}
+
+// Grid rows of a launch: one per gathered output row, or one.
+inline unsigned gemv_grid_rows(const GemvBatch& bt) { return bt.exp ? (unsigned)bt.rows : 1u; }
+
+// Zeros outputs [n0, n1) of one output row, all threads of the workgroup.
+__device__ __forceinline__ void zero_outputs(void* y, int n0, int n1, bool out_f32) {
+  for (int n = n0 + (int)threadIdx.x; n < n1; n += (int)blockDim.x) {
+    if (out_f32)
+      static_cast<float*>(y)[n] = 0.f;
+    else
+      static_cast<uint16_t*>(y)[n] = 0;
+  }
+}
+
 }  // namespace bitmm

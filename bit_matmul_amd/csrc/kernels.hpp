@@ -12,6 +12,14 @@ hipError_t launch_qmv(const uint16_t* x, const uint32_t* w, const uint16_t* scal
                       const uint16_t* biases, void* y, int64_t M, int64_t N, int64_t K, int bits,
                       bool out_f32, hipStream_t stream);
 
+// Gathered GEMV (MoE decode): output row r reads activation row token_idx[r] (row r if
+// token_idx is null) of x[T, K] and expert expert_idx[r] of w[E, N, K*bits/32], any
+// order; rows with an out-of-range id are written as zeros.
+hipError_t launch_gather_qmv(const uint16_t* x, const uint32_t* w, const uint16_t* scales,
+                             const uint16_t* biases, const int32_t* token_idx,
+                             const int32_t* expert_idx, void* y, int64_t B, int64_t N, int64_t K,
+                             int64_t E, int64_t T, int bits, bool out_f32, hipStream_t stream);
+
 // Matrix-core GEMM for M >= 8.
 hipError_t launch_qmm_mfma(const uint16_t* x, const uint32_t* w, const uint16_t* scales,
                            const uint16_t* biases, void* y, int64_t M, int64_t N, int64_t K,

@@ -37,6 +37,7 @@ struct Params {
   int out_f32;
   int steps_per_wave;  // consecutive steps each wave owns
   int total_steps;     // ceil(N / R)
+  GemvBatch bt;        // gathered rows (blockIdx.y), or none
 };
 
 constexpr int kThreads = 256;
@@ -75,9 +76,19 @@ __global__ __launch_bounds__(kThreads) void qmv_dma_kernel(Params p) {
   const int64_t rowbytes = (int64_t)K * BITS / 8;
   const int r = lane / L;             // row of the step
   const int li = lane % L;
-  const uint32_t* wq = uniform_ptr(p.w);
-  const uint16_t* sq = uniform_ptr(p.s);
-  const uint16_t* bq = uniform_ptr(p.b);
+  const uint16_t* xq = p.x;
+  const uint32_t* wq = p.w;
+  const uint16_t* sq = p.s;
+  const uint16_t* bq = p.b;
+  void* yq = p.y;
+  if (!gemv_row(p.bt, K, N, p.out_f32 != 0, xq, wq, sq, bq, yq)) {
+    const int s0 = blockIdx.x * kWaves * SPW;
+    zero_outputs(yq, min(s0 * T::R, N), min((s0 + kWaves * SPW) * T::R, N), p.out_f32 != 0);
+    return;
+  }
+  wq = uniform_ptr(wq);
+  sq = uniform_ptr(sq);
+  bq = uniform_ptr(bq);
 
   // Per-lane byte offsets of the lane's chunks, relative to the step's first row.
   uint32_t coff[C], soff[C];
@@ -119,7 +130,7 @@ __global__ __launch_bounds__(kThreads) void qmv_dma_kernel(Params p) {
     const int c = threadIdx.x + j * kThreads;
     const bool ok = c < nch;
 #pragma unroll
-    for (int u = 0; u < XU; ++u) xin[j][u] = load_u128(p.x + (int64_t)(ok ? c : 0) * T::CC + 8 * u);
+    for (int u = 0; u < XU; ++u) xin[j][u] = load_u128(xq + (int64_t)(ok ? c : 0) * T::CC + 8 * u);
   }
 
   __builtin_amdgcn_sched_barrier(0);  // activation loads first: they retire first
@@ -211,9 +222,9 @@ __global__ __launch_bounds__(kThreads) void qmv_dma_kernel(Params p) {
     const int n = step * T::R + r;
     if (li == L - 1 && n < N) {
       if (p.out_f32)
-        static_cast<float*>(p.y)[n] = v;
+        static_cast<float*>(yq)[n] = v;
       else
-        static_cast<uint16_t*>(p.y)[n] = f32_to_bf16(v);
+        static_cast<uint16_t*>(yq)[n] = f32_to_bf16(v);
     }
   };
 
@@ -249,7 +260,8 @@ hipError_t launch(Params p, hipStream_t stream) {
   p.steps_per_wave = SPW;
   const int waves = (p.total_steps + SPW - 1) / SPW;
   const int blocks = (waves + kWaves - 1) / kWaves;
-  hipLaunchKernelGGL((qmv_dma_kernel<BITS, L, C, SPW>), dim3(blocks), dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL((qmv_dma_kernel<BITS, L, C, SPW>), dim3(blocks, gemv_grid_rows(p.bt)), dim3(kThreads), 0,
+                     stream, p);
   return hipGetLastError();
 }
 

@@ -31,6 +31,7 @@ struct QmvParams {
   void* y;
   int N, K;
   int out_f32;
+  GemvBatch bt;  // gathered rows (blockIdx.y, one activation row each), or none
 };
 
 constexpr int kQmvThreads = 256;
@@ -43,6 +44,16 @@ __global__ __launch_bounds__(kQmvThreads) void qmv_kernel(QmvParams p) {
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = blockIdx.x * kQmvWaves + (threadIdx.x >> 6);
   const int n0 = wave * RPW;
+  const uint16_t* xg = p.x;
+  const uint32_t* wg = p.w;
+  const uint16_t* sg = p.s;
+  const uint16_t* bg = p.b;
+  void* yg = p.y;
+  if (!gemv_row(p.bt, p.K, p.N, p.out_f32 != 0, xg, wg, sg, bg, yg)) {
+    const int w0 = blockIdx.x * kQmvWaves * RPW;
+    zero_outputs(yg, min(w0, p.N), min(w0 + kQmvWaves * RPW, p.N), p.out_f32 != 0);
+    return;
+  }
   if (n0 >= p.N) return;  // uniform per wave
   const int nch = p.K / CC;
   const int G = p.K / kGroup;
@@ -55,9 +66,9 @@ __global__ __launch_bounds__(kQmvThreads) void qmv_kernel(QmvParams p) {
 #pragma unroll
   for (int r = 0; r < RPW; ++r) {
     const int n = min(n0 + r, p.N - 1);
-    wr[r] = p.w + (int64_t)n * wrow;
-    sr[r] = p.s + (int64_t)n * G;
-    br[r] = p.b + (int64_t)n * G;
+    wr[r] = wg + (int64_t)n * wrow;
+    sr[r] = sg + (int64_t)n * G;
+    br[r] = bg + (int64_t)n * G;
   }
 
   float acc[RPW][MR];
@@ -89,7 +100,7 @@ __global__ __launch_bounds__(kQmvThreads) void qmv_kernel(QmvParams p) {
       }
 #pragma unroll
       for (int m = 0; m < MR; ++m) {
-        const uint16_t* xp = p.x + (int64_t)m * p.K + (int64_t)cc * CC;
+        const uint16_t* xp = xg + (int64_t)m * p.K + (int64_t)cc * CC;
 #pragma unroll
         for (int u = 0; u < XU; ++u) xr[i][m][u] = load_u128(xp + 8 * u);
       }
@@ -199,9 +210,9 @@ __global__ __launch_bounds__(kQmvThreads) void qmv_kernel(QmvParams p) {
       if (lane == kWave - 1 && n < p.N) {
         const int64_t o = (int64_t)m * p.N + n;
         if (p.out_f32)
-          static_cast<float*>(p.y)[o] = v;
+          static_cast<float*>(yg)[o] = v;
         else
-          static_cast<uint16_t*>(p.y)[o] = f32_to_bf16(v);
+          static_cast<uint16_t*>(yg)[o] = f32_to_bf16(v);
       }
     }
   }
@@ -211,8 +222,8 @@ template <int BITS, int MR, int RPW, int CPL>
 hipError_t launch_one(const QmvParams& p, hipStream_t stream) {
   const int waves = (p.N + RPW - 1) / RPW;
   const int blocks = (waves + kQmvWaves - 1) / kQmvWaves;
-  hipLaunchKernelGGL((qmv_kernel<BITS, MR, RPW, CPL>), dim3(blocks), dim3(kQmvThreads), 0, stream,
-                     p);
+  hipLaunchKernelGGL((qmv_kernel<BITS, MR, RPW, CPL>), dim3(blocks, gemv_grid_rows(p.bt)),
+                     dim3(kQmvThreads), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -38,6 +38,7 @@ struct Params {
   void* y;
   int N, K;
   int out_f32;
+  GemvBatch bt;  // gathered rows (blockIdx.y), or none
 };
 
 constexpr uint32_t kNoChunk = 0x80000000u;   // outside every descriptor: reads zeros
@@ -74,9 +75,19 @@ __global__ __launch_bounds__(64 * MAXW) void qmv_split_kernel(Params p) {
   const int64_t rowbytes = (int64_t)K * BITS / 8;
   const int nblk = (N + RW - 1) / RW;
   const int stride = gridDim.x;
-  const char* wq = reinterpret_cast<const char*>(uniform_ptr(p.w));
-  const uint16_t* sq = uniform_ptr(p.s);
-  const uint16_t* bq = uniform_ptr(p.b);
+  const uint16_t* xq = p.x;
+  const uint32_t* wq0 = p.w;
+  const uint16_t* sq = p.s;
+  const uint16_t* bq = p.b;
+  void* yq = p.y;
+  if (!gemv_row(p.bt, K, N, p.out_f32 != 0, xq, wq0, sq, bq, yq)) {
+    for (int bk = blockIdx.x; bk < nblk; bk += stride)
+      zero_outputs(yq, bk * RW, min(bk * RW + RW, N), p.out_f32 != 0);
+    return;
+  }
+  const char* wq = reinterpret_cast<const char*>(uniform_ptr(wq0));
+  sq = uniform_ptr(sq);
+  bq = uniform_ptr(bq);
   const uint32_t voff = ok ? (uint32_t)(r * rowbytes + c * 16) : kNoChunk;
   const uint32_t soff = ok ? (uint32_t)((r * G + c * CC / kGroup) * 2) : kNoChunk;
 
@@ -116,7 +127,7 @@ __global__ __launch_bounds__(64 * MAXW) void qmv_split_kernel(Params p) {
 #pragma unroll
     for (int m = 0; m < MR; ++m)
 #pragma unroll
-      for (int u = 0; u < XU; ++u) xin[m][u] = load_u128(p.x + (int64_t)m * K + (int64_t)cc * CC + 8 * u);
+      for (int u = 0; u < XU; ++u) xin[m][u] = load_u128(xq + (int64_t)m * K + (int64_t)cc * CC + 8 * u);
   }
   __builtin_amdgcn_sched_barrier(0);
   load(blk, A);
@@ -211,9 +222,9 @@ __global__ __launch_bounds__(64 * MAXW) void qmv_split_kernel(Params p) {
       if (n < N) {
         const int64_t o = (int64_t)m * N + n;
         if (p.out_f32)
-          static_cast<float*>(p.y)[o] = v;
+          static_cast<float*>(yq)[o] = v;
         else
-          static_cast<uint16_t*>(p.y)[o] = f32_to_bf16(v);
+          static_cast<uint16_t*>(yq)[o] = f32_to_bf16(v);
       }
     }
   };
@@ -258,8 +269,9 @@ template <int BITS, int MR, int S>
 hipError_t launch_s(const Params& p, hipStream_t stream) {
   const int nw = (int)((chunks(p.K, BITS) + 31) / 32);
   const int nblk = (p.N + 2 * S - 1) / (2 * S);
-  const int grid = std::min(nblk, resident_blocks<BITS, MR, S>(nw));
-  hipLaunchKernelGGL((qmv_split_kernel<BITS, MR, S, max_waves(MR)>), dim3(grid), dim3(64 * nw), 0,
+  const unsigned rows = gemv_grid_rows(p.bt);
+  const int grid = std::max(1, std::min(nblk, resident_blocks<BITS, MR, S>(nw) / (int)rows));
+  hipLaunchKernelGGL((qmv_split_kernel<BITS, MR, S, max_waves(MR)>), dim3(grid, rows), dim3(64 * nw), 0,
                      stream, p);
   return hipGetLastError();
 }

@@ -164,6 +164,36 @@ class Gather:
         return 2 * self.B * self.N * self.K
 
 
+class GatherIndexed:
+    """Indexed gather: y[r,:] = x[token_idx[r],:] . dequant(w[expert_idx[r]])^T, rows in
+    any order (token_idx None: row r reads x row r)."""
+
+    def __init__(self, name, x, w, scales, biases, token_idx, expert_idx, bits):
+        self.name = name
+        self.x, self.w, self.scales, self.biases = x, w, scales, biases
+        self.token_idx, self.expert_idx = token_idx, expert_idx
+        self.bits = bits
+        self.T, self.K = x.shape
+        self.E, self.N = w.shape[0], w.shape[1]
+        self.B = expert_idx.shape[0]
+        assert w.shape == (self.E, self.N, self.K * bits // 32)
+        assert scales.shape == biases.shape == (self.E, self.N, self.K // GROUP)
+        assert expert_idx.dtype == np.int32
+        assert token_idx is None or (token_idx.shape == (self.B,) and token_idx.dtype == np.int32)
+
+    def algorithmic_bytes(self, out_bytes: int = 2) -> int:
+        """Weights of every distinct expert the rows use (streamed once), the activation
+        rows they read, the ids and the outputs."""
+        used = np.unique(self.expert_idx[(self.expert_idx >= 0) & (self.expert_idx < self.E)])
+        per_expert = (self.w[0].nbytes + self.scales[0].nbytes + self.biases[0].nbytes)
+        rows = self.T if self.token_idx is None else np.unique(self.token_idx).size
+        ids = self.expert_idx.nbytes + (0 if self.token_idx is None else self.token_idx.nbytes)
+        return (used.size * per_expert + rows * self.K * 2 + ids + self.B * self.N * out_bytes)
+
+    def flops(self) -> int:
+        return 2 * self.B * self.N * self.K
+
+
 def _dense_weights(seed: int, N: int, K: int, bits: int, sub: int = 0):
     w = random_words(rng_for(seed, TAG_Q, bits, N, K, sub), (N, K * bits // 32))
     s = random_scales(rng_for(seed, TAG_SCALE, N, K, sub), (N, K // GROUP))
@@ -246,6 +276,51 @@ def moe_gather(which: str, seed: int = 0, tokens: int = MOE_TOKENS, E: int = MOE
     s = random_scales(rng_for(seed, TAG_SCALE, E, N, K), (E, N, K // GROUP))
     b = bias_for_scales(s, bits)
     return Gather(f"gather_{which}_B{B}_E{E}_K{K}_N{N}_b{bits}", x, w, s, b, idx, bits, tok)
+
+
+def moe_decode(which: str, tokens: int = 1, seed: int = 0, E: int = MOE_E, top_k: int = MOE_TOPK,
+               hidden: int = MOE_HIDDEN, inter: int = MOE_INTER, bits: int = 4) -> GatherIndexed:
+    """MoE decode step: each of `tokens` tokens picks top_k distinct experts uniformly;
+    output rows are token-major (expert ids unsorted), B = tokens * top_k.
+
+    ``which="up"``:   K=hidden, N=inter; row r reads hidden-state row token_idx[r].
+    ``which="down"``: K=inter, N=hidden; each row reads its own activation row (a fresh
+                      N(0,1) draw [B, inter]), no token index.
+    The expert weights are the same draws as ``moe_gather``'s (one MoE layer's experts).
+    """
+    rng = rng_for(seed, TAG_ROUTE, tokens, E, top_k, 1)
+    experts = np.concatenate([rng.choice(E, top_k, replace=False) for _ in range(tokens)])
+    experts = np.ascontiguousarray(experts.astype(np.int32))
+    B = experts.shape[0]
+    if which == "up":
+        K, N = hidden, inter
+        x = to_bf16_bits(rng_for(seed, TAG_X, 6, tokens, hidden).standard_normal(size=(tokens, hidden)))
+        tok = np.repeat(np.arange(tokens, dtype=np.int32), top_k)
+    elif which == "down":
+        K, N = inter, hidden
+        x = to_bf16_bits(rng_for(seed, TAG_X2, 6, B, inter).standard_normal(size=(B, inter)))
+        tok = None
+    else:
+        raise ValueError("which must be 'up' or 'down'")
+    w = random_words(rng_for(seed, TAG_Q, bits, E, N, K), (E, N, K * bits // 32))
+    s = random_scales(rng_for(seed, TAG_SCALE, E, N, K), (E, N, K // GROUP))
+    b = bias_for_scales(s, bits)
+    return GatherIndexed(f"moe_decode_{which}_T{tokens}_B{B}_E{E}_K{K}_N{N}_b{bits}", x, w, s, b,
+                         tok, experts, bits)
+
+
+def random_indexed(T: int, B: int, E: int, N: int, K: int, bits: int, seed: int = 0,
+                   with_tokens: bool = True) -> GatherIndexed:
+    """Arbitrary indexed gather: random token and expert per row (repeats, any order)."""
+    rng = rng_for(seed, TAG_ROUTE, 9, T, B, E, N, K)
+    exp = rng.integers(0, E, B).astype(np.int32)
+    tok = rng.integers(0, T, B).astype(np.int32) if with_tokens else None
+    rows = T if with_tokens else B
+    x = to_bf16_bits(rng_for(seed, TAG_X, 9, rows, K).standard_normal(size=(rows, K)))
+    w = random_words(rng_for(seed, TAG_Q, bits, E, N, K, 9), (E, N, K * bits // 32))
+    s = random_scales(rng_for(seed, TAG_SCALE, E, N, K, 9), (E, N, K // GROUP))
+    b = bias_for_scales(s, bits)
+    return GatherIndexed(f"indexed_T{rows}_B{B}_E{E}_K{K}_N{N}_b{bits}", x, w, s, b, tok, exp, bits)
 
 
 def random_dense(M: int, N: int, K: int, bits: int, seed: int = 0, x_dist: str = "normal") -> Dense:

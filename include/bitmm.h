@@ -126,6 +126,27 @@ bitmm_status bitmm_gather_qmm(const void* x, const uint32_t* w, const void* scal
                               bitmm_out out, void* workspace, size_t workspace_bytes,
                               void* stream);
 
+/*
+ * Gathered GEMV for MoE decode. Issue #1538's correction on MoE decode (its comment
+ * "MoE decode does not route to qmm_naive") finds the decode-time experts running in
+ * dedicated per-token kernels, apart from the prefill grouped GEMM; each of their
+ * products is this one, the general GatherQMM of PR #1562 with one activation row per
+ * output row:
+ *   y[r, :] = x[t_r, :] * dequant(w[expert_idx[r]])^T for r in [0, B),
+ *   t_r = token_idx[r], or r when token_idx is NULL.
+ *   x: bf16 [T, K]; w: uint32 [E, N, K*bits/32]; scales, biases: bf16 [E, N, K/group_size];
+ *   token_idx (optional), expert_idx: int32 [B], any order, repeats allowed;
+ *   y: [B, N] of type `out`.
+ * A row whose token id is outside [0, T) or whose expert id is outside [0, E) is written
+ * as zeros. Each row streams its expert's weights once; no workspace, one launch (more
+ * only past 65535 rows). Products are exact and accumulation f32, as in bitmm_qmv.
+ */
+bitmm_status bitmm_gather_qmv(const void* x, const uint32_t* w, const void* scales,
+                              const void* biases, const int32_t* token_idx,
+                              const int32_t* expert_idx, void* y, int64_t B, int64_t N, int64_t K,
+                              int64_t E, int64_t T, int bits, int group_size, bitmm_out out,
+                              void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -44,7 +44,8 @@ def gpu_present():
 def test_exports_every_declared_function(L):
     names = header_functions()
     assert set(names) == {"bitmm_abi_version", "bitmm_status_string", "bitmm_qmv", "bitmm_qmm",
-                          "bitmm_gather_qmm_workspace_bytes", "bitmm_gather_qmm"}
+                          "bitmm_gather_qmm_workspace_bytes", "bitmm_gather_qmm",
+                          "bitmm_gather_qmv"}
     for n in names:
         assert hasattr(L, n), f"libbitmm.so does not export {n}"
 
@@ -167,6 +168,52 @@ def test_gather_validation(L, kw, expected):
             pytest.skip("fake pointers would reach a real device")
         expected = bm.BITMM_ERR_DEVICE
     assert L.bitmm_gather_qmm(*gather_args(**kw)) == expected
+
+
+def gqmv_args(**kw):
+    a = dict(x=A, w=A + 0x1000, s=A + 0x2000, b=A + 0x3000, tok=A + 0x4000, idx=A + 0x5000,
+             y=A + 0x6000, B=8, N=704, K=2816, E=128, T=1, bits=4, group=64, out=0, stream=0)
+    a.update(kw)
+    return [ctypes.c_void_p(a["x"]), ctypes.c_void_p(a["w"]), ctypes.c_void_p(a["s"]),
+            ctypes.c_void_p(a["b"]), ctypes.c_void_p(a["tok"]), ctypes.c_void_p(a["idx"]),
+            ctypes.c_void_p(a["y"]), a["B"], a["N"], a["K"], a["E"], a["T"], a["bits"],
+            a["group"], a["out"], ctypes.c_void_p(a["stream"])]
+
+
+GQMV_CASES = [
+    (dict(bits=2), bm.BITMM_ERR_UNSUPPORTED),
+    (dict(group=128), bm.BITMM_ERR_UNSUPPORTED),
+    (dict(out=7), bm.BITMM_ERR_UNSUPPORTED),
+    (dict(E=0), bm.BITMM_ERR_SHAPE),
+    (dict(K=0), bm.BITMM_ERR_SHAPE),
+    (dict(K=96), bm.BITMM_ERR_SHAPE),
+    (dict(T=-1), bm.BITMM_ERR_SHAPE),
+    (dict(B=-2), bm.BITMM_ERR_SHAPE),
+    (dict(B=1 << 31), bm.BITMM_ERR_SHAPE),
+    (dict(B=0), bm.BITMM_OK),
+    (dict(N=0, idx=0), bm.BITMM_OK),
+    (dict(idx=0), bm.BITMM_ERR_NULL),
+    (dict(w=0), bm.BITMM_ERR_NULL),
+    (dict(x=0), bm.BITMM_ERR_NULL),
+    (dict(y=0), bm.BITMM_ERR_NULL),
+    (dict(tok=A + 2), bm.BITMM_ERR_ALIGN),
+    (dict(idx=A + 6), bm.BITMM_ERR_ALIGN),
+    (dict(x=A + 8), bm.BITMM_ERR_ALIGN),
+    (dict(y=A + 1), bm.BITMM_ERR_ALIGN),
+    (dict(y=A + 2, out=1), bm.BITMM_ERR_ALIGN),
+    (dict(), None),            # token index given
+    (dict(tok=0), None),       # no token index: row r reads x row r
+    (dict(x=0, T=0), None),    # no activation rows: every row is a zero row
+]
+
+
+@pytest.mark.parametrize("kw,expected", GQMV_CASES)
+def test_gather_qmv_validation(L, kw, expected):
+    if expected is None:
+        if gpu_present():
+            pytest.skip("fake pointers would reach a real device")
+        expected = bm.BITMM_ERR_DEVICE
+    assert L.bitmm_gather_qmv(*gqmv_args(**kw)) == expected
 
 
 def test_workspace_size(L):
