@@ -19,7 +19,8 @@ for the dominant kernel (the N = 13824 GEMV), timed the same way on its own.
 Also reported: ``cpu_baseline``, the CPU oracle timed on the host cores on a
 bounded sample of the same workload, and ``suite``, every other workload of the
 hot path (the 8-bit GEMV, the prefill GEMM at M = 600 and M = 3, 4- and 8-bit,
-and the MoE expert-gathered GEMM in both orientations), timed the same way.
+the MoE expert-gathered GEMM in both orientations, and the MoE decode step's
+gathered GEMV at 1 and 4 tokens in both orientations), timed the same way.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-suite] [--no-cpu]
                        [--calibrate-copy]
@@ -93,8 +94,14 @@ class Case:
             return torch.from_numpy(np.ascontiguousarray(a).view(np.int32)).to(dev)
 
         base = [bf16(problem.x), i32(problem.w), bf16(problem.scales), bf16(problem.biases)]
+        self.ids = None
         if kind == "gather":
             base.append(i32(problem.expert_idx))
+            rows = problem.B
+        elif kind == "gather_qmv":
+            # the ids stay put: each step's rows read a different copy of every tensor
+            self.ids = (None if problem.token_idx is None else i32(problem.token_idx),
+                        i32(problem.expert_idx))
             rows = problem.B
         else:
             rows = problem.M
@@ -123,6 +130,8 @@ class Case:
             bm.bitmm_qmv(*ts, y, p.bits)
         elif self.kind == "qmm":
             bm.bitmm_qmm(*ts, y, p.bits)
+        elif self.kind == "gather_qmv":
+            bm.bitmm_gather_qmv(*ts, *self.ids, y, p.bits)
         else:
             bm.bitmm_gather_qmm(*ts, y, ws, p.bits)
 
@@ -281,7 +290,9 @@ def main():
         specs = [("qmv", lambda: I.hidden5120(1, 5120, 8)), ("qmv", lambda: I.hidden5120(1, 13824, 8)),
                  ("qmm", lambda: I.hidden5120(600, 13824, 4)), ("qmm", lambda: I.hidden5120(3, 13824, 4)),
                  ("qmm", lambda: I.hidden5120(600, 13824, 8)), ("qmm", lambda: I.hidden5120(3, 13824, 8)),
-                 ("gather", lambda: I.moe_gather("up")), ("gather", lambda: I.moe_gather("down"))]
+                 ("gather", lambda: I.moe_gather("up")), ("gather", lambda: I.moe_gather("down")),
+                 ("gather_qmv", lambda: I.moe_decode("up", 1)), ("gather_qmv", lambda: I.moe_decode("down", 1)),
+                 ("gather_qmv", lambda: I.moe_decode("up", 4)), ("gather_qmv", lambda: I.moe_decode("down", 4))]
         for kind, make in specs:
             p = make()
             c = Case(torch, p, kind, torch.bfloat16)

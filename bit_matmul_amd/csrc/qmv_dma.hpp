@@ -266,10 +266,10 @@ hipError_t launch(Params p, hipStream_t stream) {
 }
 
 // Steps per wave: the largest of 8, 4, 2, 1 that still gives every SIMD of the chip
-// at least `waves_per_cu` / 4 waves.
+// at least `waves_per_cu` / 4 waves (counting the steps of every gathered row).
 template <int BITS, int L, int C>
 hipError_t launch_spw(const Params& p, int cus, int waves_per_cu, hipStream_t stream) {
-  const int64_t steps = (p.N + (64 / L) - 1) / (64 / L);
+  const int64_t steps = (int64_t)((p.N + (64 / L) - 1) / (64 / L)) * gemv_grid_rows(p.bt);
   const int64_t want = (int64_t)cus * waves_per_cu;
   if (steps >= want * 8) return launch<BITS, L, C, 8>(p, stream);
   if (steps >= want * 4) return launch<BITS, L, C, 4>(p, stream);
