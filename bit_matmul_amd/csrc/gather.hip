@@ -22,36 +22,35 @@ constexpr int kPrepThreads = 1024;
 
 // ws[0]: 0 if the ids are valid, else 1 + first offending row.
 // ws[1 + e], e in [0, E]: first row whose id is >= e (row offsets of the experts).
+// One pass over the ids, every thread on rows t, t + 1024, ...: where the id steps up
+// from a (the previous row's id, -1 before row 0) to c, the offsets of the experts
+// a+1 .. c are that row; past the last row, the offsets of the experts after its id
+// are B. With valid ids each offset is written exactly once; with invalid ones the
+// offsets are not meaningful and the grouped GEMM does not read them.
 __global__ __launch_bounds__(kPrepThreads) void gather_prepare_kernel(const int32_t* __restrict__ idx,
                                                                       int B, int E,
                                                                       uint32_t* __restrict__ ws) {
   __shared__ int first_bad;
   if (threadIdx.x == 0) first_bad = B;
   __syncthreads();
+  int32_t* off = reinterpret_cast<int32_t*>(ws + 1);
   int mine = B;
   for (int r = threadIdx.x; r < B; r += kPrepThreads) {
-    const int e = idx[r];
-    const bool bad = e < 0 || e >= E || (r > 0 && idx[r - 1] > e);
-    if (bad) {
-      mine = r;
-      break;  // rows are visited in increasing order per thread
+    const int c = idx[r];
+    const int a = r > 0 ? idx[r - 1] : -1;
+    if (c < 0 || c >= E || a > c) {
+      mine = min(mine, r);
+      continue;
     }
+    for (int e = max(a, -1) + 1; e <= c; ++e) off[e] = r;  // a may be an invalid id
   }
+  if (B > 0 && threadIdx.x == 0) {
+    const int last = idx[B - 1];
+    for (int e = max(last, -1) + 1; e <= E; ++e) off[e] = B;
+  }
+  if (B == 0)
+    for (int e = threadIdx.x; e <= E; e += kPrepThreads) off[e] = 0;
   if (mine < B) atomicMin(&first_bad, mine);
-  // Offsets by binary search (lower bound of e); meaningful when ids are sorted and
-  // always in bounds.
-  int32_t* off = reinterpret_cast<int32_t*>(ws + 1);
-  for (int e = threadIdx.x; e <= E; e += kPrepThreads) {
-    int lo = 0, hi = B;
-    while (lo < hi) {
-      const int mid = (lo + hi) >> 1;
-      if (idx[mid] < e)
-        lo = mid + 1;
-      else
-        hi = mid;
-    }
-    off[e] = lo;
-  }
   __syncthreads();
   if (threadIdx.x == 0) ws[0] = first_bad < B ? (uint32_t)first_bad + 1u : 0u;
 }
