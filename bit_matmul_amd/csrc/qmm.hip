@@ -73,17 +73,30 @@ hipError_t launch_tile3(QmmParams p, hipStream_t stream) {
 }
 
 // 32x32x16 tile: one row of 4 waves, each with 32 weight rows and all the tile's rows
-// (blocks of 32, at most 320 rows: three activation buffers fit in LDS).
+// (blocks of 32, at most 320 rows: three activation buffers fit in LDS). When the groups
+// fit (G <= 80, G even, 4-byte aligned scale and bias arrays), each wave's scales and
+// biases are staged in LDS once (4-byte copies of its contiguous block) instead of
+// being fetched per group: at M = 600, K = 5120 that is the difference between 110 and
+// 92 us. At 320 rows the activation buffers and the staging area fill the 160 KB.
+template <int BITS, int MB>
+hipError_t launch_mb(QmmParams p, hipStream_t stream) {
+  const int G = p.K / kGroup;
+  const bool stage = G <= 80 && G % 2 == 0 && (reinterpret_cast<uintptr_t>(p.s) & 3) == 0 &&
+                     (reinterpret_cast<uintptr_t>(p.b) & 3) == 0;
+  return stage ? launch_tiles<MmTile4<BITS, MB, 4, 3, 2, 1, 80>>(p, stream)
+               : launch_tiles<MmTile4<BITS, MB, 4>>(p, stream);
+}
+
 template <int BITS>
 hipError_t launch_tile4(QmmParams p, hipStream_t stream) {
   const int64_t blocks = (p.M + 31) / 32;
   const int64_t tiles = (blocks + 9) / 10;
   const int64_t per = (blocks + tiles - 1) / tiles;
-  if (per <= 2) return launch_tiles<MmTile4<BITS, 2, 4>>(p, stream);
-  if (per <= 4) return launch_tiles<MmTile4<BITS, 4, 4>>(p, stream);
-  if (per <= 6) return launch_tiles<MmTile4<BITS, 6, 4>>(p, stream);
-  if (per <= 8) return launch_tiles<MmTile4<BITS, 8, 4>>(p, stream);
-  return launch_tiles<MmTile4<BITS, 10, 4>>(p, stream);
+  if (per <= 2) return launch_mb<BITS, 2>(p, stream);
+  if (per <= 4) return launch_mb<BITS, 4>(p, stream);
+  if (per <= 6) return launch_mb<BITS, 6>(p, stream);
+  if (per <= 8) return launch_mb<BITS, 8>(p, stream);
+  return launch_mb<BITS, 10>(p, stream);
 }
 
 }  // namespace

@@ -95,7 +95,30 @@ MFMA_SHAPES = [(8, 16, 64), (9, 100, 192), (16, 128, 128), (33, 70, 320), (130, 
                # row tiles of 32-row blocks: one group, two, three (one unrolled pass),
                # four; a full 320-row tile, a ragged one, three row tiles
                (96, 40, 64), (300, 200, 128), (65, 1000, 704), (320, 128, 192),
-               (321, 131, 256), (641, 96, 320)]
+               (321, 131, 256), (641, 96, 320),
+               # scales and biases staged in LDS up to 80 groups (G even), fetched per
+               # group beyond
+               (100, 70, 5120), (70, 66, 5248)]
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("M,K", [(200, 1024), (40, 2048)])
+def test_qmm_mfma_misaligned_scales(M, K, bits):
+    """Scale and bias arrays that are only 2-byte aligned take the per-group path."""
+    t = G.torch()
+    d = I.random_dense(M, 150, K, bits, seed=M + K)
+    x, w, s, b = G.dense_to_dev(d)
+
+    def shift(a):
+        buf = t.empty(a.numel() + 1, dtype=a.dtype, device=a.device)
+        v = buf[1:].view(a.shape)
+        v.copy_(a)
+        return v
+    s, b = shift(s), shift(b)
+    assert s.data_ptr() % 4 == 2
+    y = t.empty((d.M, d.N), dtype=t.bfloat16, device=G.dev())
+    bm.bitmm_qmm(x, w, s, b, y, bits)
+    G.assert_close(G.to_f64(y), oracle_dense(d), "bf16", f"qmm misaligned M{M} K{K} b{bits}")
 
 
 @pytest.mark.parametrize("bits", [4, 8])
