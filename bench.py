@@ -19,8 +19,9 @@ for the dominant kernel (the N = 13824 GEMV), timed the same way on its own.
 Also reported: ``cpu_baseline``, the CPU oracle timed on the host cores on a
 bounded sample of the same workload, and ``suite``, every other workload of the
 hot path (the 8-bit GEMV, the prefill GEMM at M = 600 and M = 3, 4- and 8-bit,
-the MoE expert-gathered GEMM in both orientations, and the MoE decode step's
-gathered GEMV at 1 and 4 tokens in both orientations), timed the same way.
+the MoE expert-gathered GEMM in both orientations, sorted and in routing order through
+the indexed entry point, and the MoE decode step's gathered GEMV at 1 and 4 tokens in
+both orientations), timed the same way.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-suite] [--no-cpu]
                        [--calibrate-copy]
@@ -98,7 +99,7 @@ class Case:
         if kind == "gather":
             base.append(i32(problem.expert_idx))
             rows = problem.B
-        elif kind == "gather_qmv":
+        elif kind in ("gather_qmv", "gather_indexed"):
             # the ids stay put: each step's rows read a different copy of every tensor
             self.ids = (None if problem.token_idx is None else i32(problem.token_idx),
                         i32(problem.expert_idx))
@@ -118,6 +119,9 @@ class Case:
             if kind == "gather":
                 ws = torch.empty(bm.bitmm_gather_qmm_workspace_bytes(problem.B, problem.N, problem.E),
                                  dtype=torch.uint8, device=dev)
+            elif kind == "gather_indexed":
+                ws = torch.empty(bm.bitmm_gather_qmm_indexed_workspace_bytes(problem.B, problem.N, problem.E),
+                                 dtype=torch.uint8, device=dev)
             self.sets.append((ts, y, ws))
         self.bm = bm
         self.i = 0
@@ -132,6 +136,8 @@ class Case:
             bm.bitmm_qmm(*ts, y, p.bits)
         elif self.kind == "gather_qmv":
             bm.bitmm_gather_qmv(*ts, *self.ids, y, p.bits)
+        elif self.kind == "gather_indexed":
+            bm.bitmm_gather_qmm_indexed(*ts, *self.ids, y, ws, p.bits)
         else:
             bm.bitmm_gather_qmm(*ts, y, ws, p.bits)
 
@@ -291,6 +297,8 @@ def main():
                  ("qmm", lambda: I.hidden5120(600, 13824, 4)), ("qmm", lambda: I.hidden5120(3, 13824, 4)),
                  ("qmm", lambda: I.hidden5120(600, 13824, 8)), ("qmm", lambda: I.hidden5120(3, 13824, 8)),
                  ("gather", lambda: I.moe_gather("up")), ("gather", lambda: I.moe_gather("down")),
+                 ("gather_indexed", lambda: I.moe_prefill_indexed("up")),
+                 ("gather_indexed", lambda: I.moe_prefill_indexed("down")),
                  ("gather_qmv", lambda: I.moe_decode("up", 1)), ("gather_qmv", lambda: I.moe_decode("down", 1)),
                  ("gather_qmv", lambda: I.moe_decode("up", 4)), ("gather_qmv", lambda: I.moe_decode("down", 4))]
         for kind, make in specs:

@@ -41,8 +41,9 @@ GROUP = 64
 
 __all__ = [
     "BitmmError", "lib", "bitmm_abi_version", "bitmm_status_string", "bitmm_qmv", "bitmm_qmm",
-    "bitmm_gather_qmm_workspace_bytes", "bitmm_gather_qmm", "bitmm_gather_qmv", "qmv", "qmm",
-    "gather_qmm", "gather_qmv",
+    "bitmm_gather_qmm_workspace_bytes", "bitmm_gather_qmm", "bitmm_gather_qmv",
+    "bitmm_gather_qmm_indexed_workspace_bytes", "bitmm_gather_qmm_indexed", "qmv", "qmm",
+    "gather_qmm", "gather_qmv", "gather_qmm_indexed",
 ]
 
 
@@ -84,6 +85,11 @@ def lib() -> ctypes.CDLL:
         L.bitmm_gather_qmm.restype = I
         L.bitmm_gather_qmv.argtypes = [P, P, P, P, P, P, P, I64, I64, I64, I64, I64, I, I, I, P]
         L.bitmm_gather_qmv.restype = I
+        L.bitmm_gather_qmm_indexed_workspace_bytes.argtypes = [I64, I64, I64]
+        L.bitmm_gather_qmm_indexed_workspace_bytes.restype = SZ
+        L.bitmm_gather_qmm_indexed.argtypes = [P, P, P, P, P, P, P, I64, I64, I64, I64, I64, I, I,
+                                               I, P, SZ, P]
+        L.bitmm_gather_qmm_indexed.restype = I
         _lib = L
     return _lib
 
@@ -98,6 +104,10 @@ def bitmm_status_string(status: int) -> str:
 
 def bitmm_gather_qmm_workspace_bytes(B: int, N: int, E: int) -> int:
     return int(lib().bitmm_gather_qmm_workspace_bytes(int(B), int(N), int(E)))
+
+
+def bitmm_gather_qmm_indexed_workspace_bytes(B: int, N: int, E: int) -> int:
+    return int(lib().bitmm_gather_qmm_indexed_workspace_bytes(int(B), int(N), int(E)))
 
 
 # ---------------------------------------------------------------------------
@@ -200,6 +210,37 @@ def bitmm_gather_qmm(x, w, scales, biases, expert_idx, y, workspace, bits: int,
     return y
 
 
+def bitmm_gather_qmm_indexed(x, w, scales, biases, token_idx, expert_idx, y, workspace, bits: int,
+                             group_size: int = GROUP, stream=None):
+    """y[r, :] = x[token_idx[r], :] * dequant(w[expert_idx[r]])^T (MoE prefill, rows in any
+    order, token_idx may be None); out-of-range ids give zero rows (workspace word 0 flags
+    the first)."""
+    torch = _torch()
+    T, K = x.shape
+    E, N = w.shape[0], w.shape[1]
+    B = expert_idx.shape[0]
+    dev = x.device
+    _expect(x, "x", torch.bfloat16, (T, K), dev)
+    if K % group_size:
+        raise ValueError(f"K={K} is not a multiple of group_size={group_size}")
+    _expect(w, "w", torch.int32, (E, N, K * bits // 32), dev)
+    _expect(scales, "scales", torch.bfloat16, (E, N, K // group_size), dev)
+    _expect(biases, "biases", torch.bfloat16, (E, N, K // group_size), dev)
+    _expect(expert_idx, "expert_idx", torch.int32, (B,), dev)
+    if token_idx is not None:
+        _expect(token_idx, "token_idx", torch.int32, (B,), dev)
+    _expect(y, "y", y.dtype, (B, N), dev)
+    if workspace.dtype != torch.uint8 or workspace.device != dev or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 tensor on the same device")
+    st = lib().bitmm_gather_qmm_indexed(_ptr(x), _ptr(w), _ptr(scales), _ptr(biases),
+                                        _ptr(token_idx), _ptr(expert_idx), _ptr(y), B, N, K, E, T,
+                                        int(bits), int(group_size), _out_code(y), _ptr(workspace),
+                                        workspace.numel(), _stream_ptr(stream, dev))
+    if st != BITMM_OK:
+        raise BitmmError(st, "bitmm_gather_qmm_indexed")
+    return y
+
+
 def bitmm_gather_qmv(x, w, scales, biases, token_idx, expert_idx, y, bits: int,
                      group_size: int = GROUP, stream=None):
     """y[r, :] = x[token_idx[r], :] * dequant(w[expert_idx[r]])^T (MoE decode); token_idx
@@ -262,3 +303,17 @@ def gather_qmv(x, w, scales, biases, token_idx, expert_idx, bits: int, out_dtype
     y = torch.empty((expert_idx.shape[0], w.shape[1]), dtype=out_dtype or torch.bfloat16,
                     device=x.device)
     return bitmm_gather_qmv(x, w, scales, biases, token_idx, expert_idx, y, bits, stream=stream)
+
+
+def gather_qmm_indexed(x, w, scales, biases, token_idx, expert_idx, bits: int, out_dtype=None,
+                       workspace=None, stream=None):
+    """Returns (y, workspace); workspace word 0 flags the first row with an out-of-range id."""
+    torch = _torch()
+    B, N, E = expert_idx.shape[0], w.shape[1], w.shape[0]
+    y = torch.empty((B, N), dtype=out_dtype or torch.bfloat16, device=x.device)
+    if workspace is None:
+        workspace = torch.empty(max(bitmm_gather_qmm_indexed_workspace_bytes(B, N, E), 256),
+                                dtype=torch.uint8, device=x.device)
+    bitmm_gather_qmm_indexed(x, w, scales, biases, token_idx, expert_idx, y, workspace, bits,
+                             stream=stream)
+    return y, workspace

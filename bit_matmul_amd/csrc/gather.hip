@@ -55,6 +55,93 @@ __global__ __launch_bounds__(kPrepThreads) void gather_prepare_kernel(const int3
   if (threadIdx.x == 0) ws[0] = first_bad < B ? (uint32_t)first_bad + 1u : 0u;
 }
 
+// Indexed form: rows in any order, an optional token index. One workgroup builds a
+// permutation that groups the rows by expert (a counting sort; the order of rows within
+// an expert does not matter, since every output row is computed on its own) and zeros
+// the output rows whose token or expert id is out of range. Workspace words:
+//   [0]                 0, or 1 + the first row with an out-of-range id;
+//   [1 .. E+1]          offsets: expert e owns perm[off[e] .. off[e+1]);
+//   [E+2 .. E+2+B)      perm: output rows grouped by expert (invalid rows at the end).
+constexpr int kMaxIndexedExperts = 8192;  // per-expert counters live in LDS
+
+// Exclusive prefix sum of v[0 .. n) in LDS, in place, by all kPrepThreads threads:
+// each thread sums a run of entries, the run totals are scanned within each wave with
+// lane shifts and across the waves by one wave, then each thread rewrites its run.
+__device__ void block_exclusive_scan(int* v, int n, int* part) {
+  constexpr int kWaves = kPrepThreads / 64;
+  const int per = (n + kPrepThreads - 1) / kPrepThreads;
+  const int b0 = min(n, (int)threadIdx.x * per), b1 = min(n, b0 + per);
+  int t = 0;
+  for (int i = b0; i < b1; ++i) t += v[i];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int inc = t;
+  for (int d = 1; d < 64; d <<= 1) {
+    const int u = __shfl_up(inc, d, 64);
+    if (lane >= d) inc += u;
+  }
+  if (lane == 63) part[wave] = inc;
+  __syncthreads();
+  if (wave == 0) {
+    int w = lane < kWaves ? part[lane] : 0;
+    for (int d = 1; d < kWaves; d <<= 1) {
+      const int u = __shfl_up(w, d, 64);
+      if (lane >= d) w += u;
+    }
+    if (lane < kWaves) part[kWaves + lane] = w;  // inclusive sums of the wave totals
+  }
+  __syncthreads();
+  int acc = (wave > 0 ? part[kWaves + wave - 1] : 0) + inc - t;
+  for (int i = b0; i < b1; ++i) {
+    const int c = v[i];
+    v[i] = acc;
+    acc += c;
+  }
+  __syncthreads();
+}
+
+__global__ __launch_bounds__(kPrepThreads) void gather_sort_kernel(const int32_t* __restrict__ tok,
+                                                                   const int32_t* __restrict__ exp,
+                                                                   int B, int E, int T, int N,
+                                                                   int out_f32, void* __restrict__ y,
+                                                                   uint32_t* __restrict__ ws) {
+  __shared__ int cnt[kMaxIndexedExperts + 1];
+  __shared__ int part[kPrepThreads];
+  __shared__ int first_bad;
+  for (int e = threadIdx.x; e <= E; e += kPrepThreads) cnt[e] = 0;
+  if (threadIdx.x == 0) first_bad = B;
+  __syncthreads();
+  int mine = B;
+  for (int r = threadIdx.x; r < B; r += kPrepThreads) {
+    const int e = exp[r];
+    const int t = tok ? tok[r] : r;
+    const bool ok = e >= 0 && e < E && t >= 0 && t < T;
+    atomicAdd(&cnt[ok ? e : E], 1);
+    if (!ok) mine = min(mine, r);
+  }
+  if (mine < B) atomicMin(&first_bad, mine);
+  __syncthreads();
+  block_exclusive_scan(cnt, E + 1, part);  // cnt[e] = first slot of expert e
+  int32_t* off = reinterpret_cast<int32_t*>(ws + 1);
+  int32_t* perm = reinterpret_cast<int32_t*>(ws + 2 + E);
+  for (int e = threadIdx.x; e <= E; e += kPrepThreads) off[e] = cnt[e];
+  __syncthreads();
+  for (int r = threadIdx.x; r < B; r += kPrepThreads) {
+    const int e = exp[r];
+    const int t = tok ? tok[r] : r;
+    const bool ok = e >= 0 && e < E && t >= 0 && t < T;
+    perm[atomicAdd(&cnt[ok ? e : E], 1)] = r;
+    if (!ok) {
+      for (int n = 0; n < N; ++n) {
+        if (out_f32)
+          static_cast<float*>(y)[(int64_t)r * N + n] = 0.f;
+        else
+          static_cast<uint16_t*>(y)[(int64_t)r * N + n] = 0;
+      }
+    }
+  }
+  if (threadIdx.x == 0) ws[0] = first_bad < B ? (uint32_t)first_bad + 1u : 0u;
+}
+
 struct GatherParams {
   const uint16_t* x;
   const uint32_t* w;
@@ -62,7 +149,8 @@ struct GatherParams {
   const uint16_t* b;
   void* y;
   const uint32_t* ws;
-  int B, N, K, E;
+  const int32_t* tok;  // indexed form: token per output row (or null)
+  int B, N, K, E, T;
   int tiles_n;
   int out_f32;
 };
@@ -117,6 +205,40 @@ __global__ __launch_bounds__(T::THREADS) void gather_qmm_kernel(GatherParams p) 
   }
 }
 
+// Indexed form: the rows of expert e are perm[off[e] .. off[e+1]); the tile gathers
+// their activation rows (through the token index) and scatters its output rows.
+template <int BITS, typename T>
+__global__ __launch_bounds__(T::THREADS) void gather_qmm_indexed_kernel(GatherParams p) {
+  __shared__ __attribute__((aligned(16))) char lds[T::LDS_BYTES];
+  const int L = xcd_remap(blockIdx.x, p.E * p.tiles_n);
+  const int e = L / p.tiles_n;
+  const int tn = L % p.tiles_n;
+  const int n0 = tn * T::BN;
+  const int32_t* off = reinterpret_cast<const int32_t*>(p.ws + 1);
+  const int32_t* perm = reinterpret_cast<const int32_t*>(p.ws + 2 + p.E);
+  const int r_begin = off[e];
+  const int r_end = off[e + 1];
+  if (r_begin >= r_end) return;
+  const int64_t words = (int64_t)p.K * BITS / 32;
+  const int64_t groups = p.K / kGroup;
+  const uint32_t* we = p.w + (int64_t)e * p.N * words;
+  const uint16_t* se = p.s + (int64_t)e * p.N * groups;
+  const uint16_t* be = p.b + (int64_t)e * p.N * groups;
+  for (int r0 = r_begin; r0 < r_end; r0 += T::BM) {
+    if (r0 > r_begin) __syncthreads();  // LDS is reused by the next row block
+    const int rows = min(T::BM, r_end - r0);
+    T::run(p.x, rows, we, se, be, n0, p.N, p.K, p.y, p.out_f32 != 0, lds, perm + r0, p.tok, p.T);
+  }
+}
+
+template <int BITS, typename T>
+hipError_t launch_indexed(GatherParams p, hipStream_t stream) {
+  p.tiles_n = (p.N + T::BN - 1) / T::BN;
+  hipLaunchKernelGGL((gather_qmm_indexed_kernel<BITS, T>), dim3(p.E * p.tiles_n), dim3(T::THREADS), 0,
+                     stream, p);
+  return hipGetLastError();
+}
+
 template <int BITS, typename T>
 hipError_t launch_grouped(GatherParams p, hipStream_t stream) {
   p.tiles_n = (p.N + T::BN - 1) / T::BN;
@@ -127,30 +249,38 @@ hipError_t launch_grouped(GatherParams p, hipStream_t stream) {
 
 // Scales and biases staged in LDS once per workgroup when the wave's block fits (G <= 48),
 // with 4-byte copies when G is even and both arrays 4-byte aligned.
-template <int BITS, int MB>
+template <int BITS, typename T, bool RMAP>
+hipError_t launch_form(GatherParams p, hipStream_t stream) {
+  if constexpr (RMAP)
+    return launch_indexed<BITS, T>(p, stream);
+  else
+    return launch_grouped<BITS, T>(p, stream);
+}
+
+template <int BITS, int MB, bool RMAP>
 hipError_t launch_sb(GatherParams p, hipStream_t stream) {
   const int G = p.K / kGroup;
   const bool wide = G % 2 == 0 && (reinterpret_cast<uintptr_t>(p.s) & 3) == 0 &&
                     (reinterpret_cast<uintptr_t>(p.b) & 3) == 0;
   if (G <= 12)
-    return wide ? launch_grouped<BITS, MmTile4<BITS, MB, 4, 3, 2, 1, 12>>(p, stream)
-                : launch_grouped<BITS, MmTile4<BITS, MB, 4, 3, 2, 2, 12>>(p, stream);
+    return wide ? launch_form<BITS, MmTile4<BITS, MB, 4, 3, 2, 1, 12, RMAP>, RMAP>(p, stream)
+                : launch_form<BITS, MmTile4<BITS, MB, 4, 3, 2, 2, 12, RMAP>, RMAP>(p, stream);
   if (G <= 48)
-    return wide ? launch_grouped<BITS, MmTile4<BITS, MB, 4, 3, 2, 1, 48>>(p, stream)
-                : launch_grouped<BITS, MmTile4<BITS, MB, 4, 3, 2, 2, 48>>(p, stream);
-  return launch_grouped<BITS, MmTile4<BITS, MB, 4>>(p, stream);
+    return wide ? launch_form<BITS, MmTile4<BITS, MB, 4, 3, 2, 1, 48, RMAP>, RMAP>(p, stream)
+                : launch_form<BITS, MmTile4<BITS, MB, 4, 3, 2, 2, 48, RMAP>, RMAP>(p, stream);
+  return launch_form<BITS, MmTile4<BITS, MB, 4, 3, 2, 0, 0, RMAP>, RMAP>(p, stream);
 }
 
 // One row of 4 waves, each with 32 weight rows: every expert's weights are dequantized
 // once per column block. Row blocks of 32 per tile from the mean rows per expert, with
 // slack for the spread of the routing; experts with more rows loop over row tiles.
-template <int BITS>
+template <int BITS, bool RMAP>
 hipError_t launch_tile4(GatherParams p, hipStream_t stream) {
   const int64_t mean = p.E > 0 ? (p.B + p.E - 1) / p.E : p.B;
   const int64_t blocks = (mean + mean / 4 + 31) / 32;
-  if (blocks <= 1) return launch_sb<BITS, 1>(p, stream);
-  if (blocks <= 2) return launch_sb<BITS, 2>(p, stream);
-  return launch_sb<BITS, 4>(p, stream);
+  if (blocks <= 1) return launch_sb<BITS, 1, RMAP>(p, stream);
+  if (blocks <= 2) return launch_sb<BITS, 2, RMAP>(p, stream);
+  return launch_sb<BITS, 4, RMAP>(p, stream);
 }
 
 }  // namespace
@@ -176,13 +306,50 @@ hipError_t launch_gather_qmm(const uint16_t* x, const uint32_t* w, const uint16_
   p.b = biases;
   p.y = y;
   p.ws = ws;
+  p.tok = nullptr;
   p.B = (int)B;
   p.N = (int)N;
   p.K = (int)K;
   p.E = (int)E;
+  p.T = (int)B;
   p.tiles_n = 0;
   p.out_f32 = out_f32 ? 1 : 0;
-  return bits == 4 ? launch_tile4<4>(p, stream) : launch_tile4<8>(p, stream);
+  return bits == 4 ? launch_tile4<4, false>(p, stream) : launch_tile4<8, false>(p, stream);
+}
+
+size_t gather_indexed_workspace_bytes(int64_t B, int64_t E) {
+  const size_t raw = (size_t)(E + 2 + B) * sizeof(uint32_t);
+  return (raw + 255) / 256 * 256;
+}
+
+int64_t gather_indexed_max_experts() { return kMaxIndexedExperts; }
+
+hipError_t launch_gather_qmm_indexed(const uint16_t* x, const uint32_t* w, const uint16_t* scales,
+                                     const uint16_t* biases, const int32_t* token_idx,
+                                     const int32_t* expert_idx, void* y, int64_t B, int64_t N,
+                                     int64_t K, int64_t E, int64_t T, int bits, bool out_f32,
+                                     void* workspace, hipStream_t stream) {
+  uint32_t* ws = static_cast<uint32_t*>(workspace);
+  hipLaunchKernelGGL(gather_sort_kernel, dim3(1), dim3(kPrepThreads), 0, stream, token_idx,
+                     expert_idx, (int)B, (int)E, (int)T, (int)N, out_f32 ? 1 : 0, y, ws);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  GatherParams p;
+  p.x = x;
+  p.w = w;
+  p.s = scales;
+  p.b = biases;
+  p.y = y;
+  p.ws = ws;
+  p.tok = token_idx;
+  p.B = (int)B;
+  p.N = (int)N;
+  p.K = (int)K;
+  p.E = (int)E;
+  p.T = (int)T;
+  p.tiles_n = 0;
+  p.out_f32 = out_f32 ? 1 : 0;
+  return bits == 4 ? launch_tile4<4, true>(p, stream) : launch_tile4<8, true>(p, stream);
 }
 
 }  // namespace bitmm

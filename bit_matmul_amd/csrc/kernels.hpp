@@ -33,4 +33,14 @@ hipError_t launch_gather_qmm(const uint16_t* x, const uint32_t* w, const uint16_
                              int64_t B, int64_t N, int64_t K, int64_t E, int bits, bool out_f32,
                              void* workspace, hipStream_t stream);
 
+// Indexed GatherQMM (rows in any order, optional token index): a counting sort of the
+// rows by expert into the workspace, then the grouped GEMM over the sorted rows.
+size_t gather_indexed_workspace_bytes(int64_t B, int64_t E);
+int64_t gather_indexed_max_experts();
+hipError_t launch_gather_qmm_indexed(const uint16_t* x, const uint32_t* w, const uint16_t* scales,
+                                     const uint16_t* biases, const int32_t* token_idx,
+                                     const int32_t* expert_idx, void* y, int64_t B, int64_t N,
+                                     int64_t K, int64_t E, int64_t T, int bits, bool out_f32,
+                                     void* workspace, hipStream_t stream);
+
 }  // namespace bitmm

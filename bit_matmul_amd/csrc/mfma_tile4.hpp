@@ -57,7 +57,10 @@ __device__ __forceinline__ void static_for(F&& f) {
 //   2: the same with 2-byte copies (each value in a 4-byte LDS slot), any alignment.
 // A per-group load touches one cache line per weight row; the staged copies touch one
 // or two per 64 values. GMAX is the largest G the staging area holds (SBM != 0).
-template <int BITS, int MB, int WN, int PD = 3, int XD = 2, int SBM = 0, int GMAX = 0>
+// RMAP: tile rows are gathered. Tile row i is output row perm[i] of y[., N], and it
+// reads activation row tok[perm[i]] of x[T, K] (row perm[i] when tok is null); without
+// RMAP, tile row i is row i of both x_rows and y_rows.
+template <int BITS, int MB, int WN, int PD = 3, int XD = 2, int SBM = 0, int GMAX = 0, bool RMAP = false>
 struct MmTile4 {
   static constexpr int WAVES = WN;
   static constexpr int THREADS = 64 * WAVES;
@@ -117,7 +120,9 @@ struct MmTile4 {
   __device__ static void run(const uint16_t* __restrict__ x_rows_in, int rows_in,
                              const uint32_t* __restrict__ w_in, const uint16_t* __restrict__ sc_in,
                              const uint16_t* __restrict__ bi_in, int n0_in, int N, int K,
-                             void* __restrict__ y_rows, bool out_f32, char* lds) {
+                             void* __restrict__ y_rows, bool out_f32, char* lds,
+                             const int32_t* __restrict__ perm = nullptr,
+                             const int32_t* __restrict__ tok = nullptr, int T = 0) {
     const uint16_t* x_rows = uniform_ptr(x_rows_in);
     const uint32_t* w = uniform_ptr(w_in);
     const uint16_t* sc = uniform_ptr(sc_in);
@@ -140,7 +145,7 @@ struct MmTile4 {
     // Descriptors for the whole K loop. Out-of-range rows (activation rows past `rows`,
     // weight rows past N) sit in the checked per-lane offset and read as zeros; the
     // group offset, always inside a row, travels in the scalar offset.
-    const __amdgpu_buffer_rsrc_t rx = make_rsrc(x_rows, (int64_t)rows * K * 2);
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(x_rows, (int64_t)(RMAP ? T : rows) * K * 2);
     const __amdgpu_buffer_rsrc_t rw =
         make_rsrc(reinterpret_cast<const char*>(w) + (int64_t)col0 * rowbytes, (int64_t)(N - col0) * rowbytes);
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(sc + (int64_t)col0 * G, (int64_t)(N - col0) * G * 2);
@@ -149,7 +154,18 @@ struct MmTile4 {
 #pragma unroll
     for (int k = 0; k < XC; ++k) {
       const int I = wave + k * WAVES;
-      xoff[k] = (uint32_t)(dma_row(I, lane) * K * 2 + dma_chunk(I, lane) * 16);
+      const int tr = dma_row(I, lane);
+      if constexpr (RMAP) {
+        // Gathered row: its activation row; tile rows past `rows` read nothing.
+        int src = 0;
+        if (tr < rows) {
+          src = perm[tr];
+          if (tok) src = tok[src];
+        }
+        xoff[k] = tr < rows ? (uint32_t)(src * K * 2 + dma_chunk(I, lane) * 16) : 0x80000000u;
+      } else {
+        xoff[k] = (uint32_t)(tr * K * 2 + dma_chunk(I, lane) * 16);
+      }
     }
     const uint32_t woff = (uint32_t)(lc * rowbytes + lh * 16 * WV);
     const uint32_t soff = (uint32_t)(lc * G * 2);
@@ -415,7 +431,7 @@ struct MmTile4 {
         const int r = 16 * t + (elane >> 2);
         const u32x4_t v = *reinterpret_cast<const u32x4_t*>(tile + (r ^ ((r >> 2) & 1)) * 64 + (elane & 3) * 16);
         if (r < rows)
-          *reinterpret_cast<u32x4_t*>(static_cast<char*>(y_rows) + ((int64_t)r * N + col0 + (elane & 3) * 8) * 2) = v;
+          *reinterpret_cast<u32x4_t*>(static_cast<char*>(y_rows) + ((int64_t)(RMAP ? perm[r] : r) * N + col0 + (elane & 3) * 8) * 2) = v;
       }
     } else if (col < N) {
 #pragma unroll
@@ -424,7 +440,7 @@ struct MmTile4 {
         for (int j = 0; j < 16; ++j) {
           const int r = mb * 32 + 8 * (j >> 2) + 4 * elh + (j & 3);
           if (r < rows) {
-            const int64_t o = (int64_t)r * N + col;
+            const int64_t o = (int64_t)(RMAP ? perm[r] : r) * N + col;
             if (out_f32)
               static_cast<float*>(y_rows)[o] = acc[mb][j];
             else

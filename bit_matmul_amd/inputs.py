@@ -278,6 +278,31 @@ def moe_gather(which: str, seed: int = 0, tokens: int = MOE_TOKENS, E: int = MOE
     return Gather(f"gather_{which}_B{B}_E{E}_K{K}_N{N}_b{bits}", x, w, s, b, idx, bits, tok)
 
 
+def moe_prefill_indexed(which: str, seed: int = 0, tokens: int = MOE_TOKENS, E: int = MOE_E,
+                        top_k: int = MOE_TOPK, hidden: int = MOE_HIDDEN, inter: int = MOE_INTER,
+                        bits: int = 4) -> GatherIndexed:
+    """MoE prefill as the routing produces it: rows token-major (expert ids unsorted).
+
+    ``which="up"``:   x = the hidden states [tokens, hidden], each row reads its token's
+                      row through the token index (no replicas).
+    ``which="down"``: x = one activation row per output row [B, inter], no token index.
+    Same routing, activations and weights as ``moe_gather``, so each output row equals
+    the corresponding row of the sorted problem.
+    """
+    g = moe_gather(which, seed, tokens, E, top_k, hidden, inter, bits)
+    order = np.argsort(g.token_of_row.astype(np.int64) * (E + 1) + g.expert_idx, kind="stable")
+    exp = np.ascontiguousarray(g.expert_idx[order])
+    if which == "up":
+        x = np.empty((tokens, g.K), dtype=np.uint16)
+        x[g.token_of_row] = g.x
+        tok = np.ascontiguousarray(g.token_of_row[order])
+    else:
+        x = np.ascontiguousarray(g.x[order])
+        tok = None
+    return GatherIndexed(f"gather_indexed_{which}_B{g.B}_E{E}_K{g.K}_N{g.N}_b{bits}", x, g.w,
+                         g.scales, g.biases, tok, exp, bits)
+
+
 def moe_decode(which: str, tokens: int = 1, seed: int = 0, E: int = MOE_E, top_k: int = MOE_TOPK,
                hidden: int = MOE_HIDDEN, inter: int = MOE_INTER, bits: int = 4) -> GatherIndexed:
     """MoE decode step: each of `tokens` tokens picks top_k distinct experts uniformly;

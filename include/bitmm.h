@@ -127,6 +127,37 @@ bitmm_status bitmm_gather_qmm(const void* x, const uint32_t* w, const void* scal
                               void* stream);
 
 /*
+ * Bytes of device workspace bitmm_gather_qmm_indexed needs for B rows, N columns and E
+ * experts (a multiple of 256; 0 if an argument is negative or E < 1).
+ */
+size_t bitmm_gather_qmm_indexed_workspace_bytes(int64_t B, int64_t N, int64_t E);
+
+/*
+ * Indexed expert-gathered GEMM: the general GatherQMM of PR #1562 (its MoE layer
+ * passes the activation rows through an index rather than replicating them per
+ * expert), with rows in any order:
+ *   y[r, :] = x[t_r, :] * dequant(w[expert_idx[r]])^T for r in [0, B),
+ *   t_r = token_idx[r], or r when token_idx is NULL.
+ *   x: bf16 [T, K]; w: uint32 [E, N, K*bits/32]; scales, biases: bf16 [E, N, K/group_size];
+ *   token_idx (optional), expert_idx: int32 [B]; y: [B, N] of type `out`.
+ * A first kernel groups the rows by expert (a counting sort into the workspace) and
+ * writes zeros to every row whose token id is outside [0, T) or expert id outside
+ * [0, E); the grouped GEMM then runs over the grouped rows, reading each activation row
+ * through the index. Workspace word 0 (uint32) receives 0, or 1 + the first row with an
+ * out-of-range id. `workspace`: caller-owned device memory of at least
+ * bitmm_gather_qmm_indexed_workspace_bytes(B, N, E) bytes, 16-byte aligned, no
+ * initialisation needed; two calls sharing it must be ordered on one stream.
+ * Limits (else BITMM_ERR_UNSUPPORTED): E <= 8192; T * K * 2 < 2^31.
+ * Precision as bitmm_gather_qmm.
+ */
+bitmm_status bitmm_gather_qmm_indexed(const void* x, const uint32_t* w, const void* scales,
+                                      const void* biases, const int32_t* token_idx,
+                                      const int32_t* expert_idx, void* y, int64_t B, int64_t N,
+                                      int64_t K, int64_t E, int64_t T, int bits, int group_size,
+                                      bitmm_out out, void* workspace, size_t workspace_bytes,
+                                      void* stream);
+
+/*
  * Gathered GEMV for MoE decode. Issue #1538's correction on MoE decode (its comment
  * "MoE decode does not route to qmm_naive") finds the decode-time experts running in
  * dedicated per-token kernels, apart from the prefill grouped GEMM; each of their

@@ -45,7 +45,8 @@ def test_exports_every_declared_function(L):
     names = header_functions()
     assert set(names) == {"bitmm_abi_version", "bitmm_status_string", "bitmm_qmv", "bitmm_qmm",
                           "bitmm_gather_qmm_workspace_bytes", "bitmm_gather_qmm",
-                          "bitmm_gather_qmv"}
+                          "bitmm_gather_qmv", "bitmm_gather_qmm_indexed_workspace_bytes",
+                          "bitmm_gather_qmm_indexed"}
     for n in names:
         assert hasattr(L, n), f"libbitmm.so does not export {n}"
 
@@ -214,6 +215,59 @@ def test_gather_qmv_validation(L, kw, expected):
             pytest.skip("fake pointers would reach a real device")
         expected = bm.BITMM_ERR_DEVICE
     assert L.bitmm_gather_qmv(*gqmv_args(**kw)) == expected
+
+
+def gidx_args(**kw):
+    a = dict(x=A, w=A + 0x1000, s=A + 0x2000, b=A + 0x3000, tok=A + 0x4000, idx=A + 0x5000,
+             y=A + 0x6000, B=4584, N=704, K=2816, E=128, T=573, bits=4, group=64, out=0,
+             ws=A + 0x7000, ws_bytes=1 << 20, stream=0)
+    a.update(kw)
+    return [ctypes.c_void_p(a["x"]), ctypes.c_void_p(a["w"]), ctypes.c_void_p(a["s"]),
+            ctypes.c_void_p(a["b"]), ctypes.c_void_p(a["tok"]), ctypes.c_void_p(a["idx"]),
+            ctypes.c_void_p(a["y"]), a["B"], a["N"], a["K"], a["E"], a["T"], a["bits"],
+            a["group"], a["out"], ctypes.c_void_p(a["ws"]), a["ws_bytes"],
+            ctypes.c_void_p(a["stream"])]
+
+
+GIDX_CASES = [
+    (dict(bits=3), bm.BITMM_ERR_UNSUPPORTED),
+    (dict(group=32), bm.BITMM_ERR_UNSUPPORTED),
+    (dict(out=2), bm.BITMM_ERR_UNSUPPORTED),
+    (dict(E=8193), bm.BITMM_ERR_UNSUPPORTED),
+    (dict(T=1 << 20, K=1024), bm.BITMM_ERR_UNSUPPORTED),
+    (dict(E=0), bm.BITMM_ERR_SHAPE),
+    (dict(K=100), bm.BITMM_ERR_SHAPE),
+    (dict(T=-1), bm.BITMM_ERR_SHAPE),
+    (dict(B=-1), bm.BITMM_ERR_SHAPE),
+    (dict(B=0), bm.BITMM_OK),
+    (dict(N=0), bm.BITMM_OK),
+    (dict(idx=0), bm.BITMM_ERR_NULL),
+    (dict(y=0), bm.BITMM_ERR_NULL),
+    (dict(ws=0), bm.BITMM_ERR_WORKSPACE),
+    (dict(ws_bytes=4 * (4584 + 130) - 1), bm.BITMM_ERR_WORKSPACE),
+    (dict(ws=A + 4), bm.BITMM_ERR_ALIGN),
+    (dict(tok=A + 1), bm.BITMM_ERR_ALIGN),
+    (dict(w=A + 4), bm.BITMM_ERR_ALIGN),
+    (dict(), None),
+    (dict(tok=0, T=4584), None),
+]
+
+
+@pytest.mark.parametrize("kw,expected", GIDX_CASES)
+def test_gather_qmm_indexed_validation(L, kw, expected):
+    if expected is None:
+        if gpu_present():
+            pytest.skip("fake pointers would reach a real device")
+        expected = bm.BITMM_ERR_DEVICE
+    assert L.bitmm_gather_qmm_indexed(*gidx_args(**kw)) == expected
+
+
+def test_indexed_workspace_size(L):
+    ws = bm.bitmm_gather_qmm_indexed_workspace_bytes
+    assert ws(4584, 704, 128) >= 4 * (4584 + 128 + 2)
+    assert ws(4584, 704, 128) % 256 == 0
+    assert ws(0, 1, 1) > 0
+    assert ws(-1, 1, 1) == 0 and ws(1, 1, 0) == 0
 
 
 def test_workspace_size(L):
