@@ -6,9 +6,10 @@
 // chunks are the same in every step, and the R rows of a step are one contiguous
 // span of W, fetched by C loads of 1 KB per wave (the fastest HBM access shape).
 //
-// Each wave owns consecutive steps and keeps a ring of five in registers: the
-// loads of step i+4 are issued before step i is computed, so four steps (about
-// 20 KB at K = 5120) are in flight per wave. The activations (the same for every
+// Each wave owns consecutive steps and keeps up to five in registers: with one or two
+// steps per wave all of its loads go out first; with more, the loads of step i+4 are
+// issued before step i is computed, so four steps (about 20 KB at K = 5120) are in
+// flight per wave. The activations (the same for every
 // row) are prepared once per workgroup in LDS and then held in registers. Loads go through buffer descriptors
 // over the rows that exist: rows past N, and chunks past the end of a row, read as
 // zeros (their scale and bias too, so they add nothing).
@@ -49,7 +50,10 @@ struct Cfg {
   static constexpr int R = 64 / L;       // rows per step
   static constexpr int CC = 128 / BITS;  // codes per 16-byte chunk
   static constexpr int LOADS = 3 * C;    // load instructions per step (codes, scales, biases)
-  static constexpr int D = SPW < 5 ? SPW : 5;  // steps in flight at once (at most 4 ahead)
+  // Steps in flight at once: up to 2 steps per wave every load goes out before the
+  // activations are prepared (the memory pipe fills from the first cycle); beyond, at
+  // most 4 steps ahead (register budget).
+  static constexpr int D = SPW <= 2 ? SPW + 1 : (SPW < 5 ? SPW : 5);
   static constexpr int XCH = 64 * C;     // activation chunks held in LDS (covers L * C)
   // Activations per chunk in LDS: 4-bit 16 bf16 pairs matched to nibble pairs (64 B);
   // 8-bit 16 f32 (64 B). Stored as 4 planes of 16 bytes, plane u of chunk c at
