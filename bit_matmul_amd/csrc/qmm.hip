@@ -1,8 +1,7 @@
 // Dense prefill GEMM on the matrix cores (M >= 8): y[M, N] = x[M, K] * dequant(w)^T.
 // The epic's kernel table puts the prefill quantized GEMM at 82% of GPU time; the
-// tile itself lives in mfma_tile3.hpp.
+// tile itself lives in mfma_tile4.hpp.
 #include "kernels.hpp"
-#include "mfma_tile3.hpp"
 #include "mfma_tile4.hpp"
 
 namespace bitmm {
@@ -51,27 +50,6 @@ hipError_t launch_tiles(QmmParams p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Pipelined tile: one row of 4 waves, each with 32 weight rows (columns of y) and
-// all the tile's activation rows, so a weight is dequantized once per row tile.
-// As few row tiles as fit in LDS (at most 320 rows), each as full as possible.
-template <int BITS>
-hipError_t launch_tile3(QmmParams p, hipStream_t stream) {
-  const int64_t blocks = (p.M + 15) / 16;
-  const int64_t tiles = (blocks + 19) / 20;
-  const int64_t per = (blocks + tiles - 1) / tiles;
-  switch (per) {
-    case 1: return launch_tiles<MmTile3<BITS, 1, 2, 1, 4>>(p, stream);
-    case 2: return launch_tiles<MmTile3<BITS, 2, 2, 1, 4>>(p, stream);
-    case 3: return launch_tiles<MmTile3<BITS, 3, 2, 1, 4>>(p, stream);
-    case 4: return launch_tiles<MmTile3<BITS, 4, 2, 1, 4>>(p, stream);
-    default: break;
-  }
-  if (per <= 8) return launch_tiles<MmTile3<BITS, 8, 2, 1, 4>>(p, stream);
-  if (per <= 12) return launch_tiles<MmTile3<BITS, 12, 2, 1, 4>>(p, stream);
-  if (per <= 16) return launch_tiles<MmTile3<BITS, 16, 2, 1, 4>>(p, stream);
-  return launch_tiles<MmTile3<BITS, 20, 2, 1, 4>>(p, stream);
-}
-
 // 32x32x16 tile: one row of 4 waves, each with 32 weight rows and all the tile's rows
 // (blocks of 32, at most 320 rows: three activation buffers fit in LDS). When the groups
 // fit (G <= 80, G even, 4-byte aligned scale and bias arrays), each wave's scales and
@@ -92,6 +70,7 @@ hipError_t launch_tile4(QmmParams p, hipStream_t stream) {
   const int64_t blocks = (p.M + 31) / 32;
   const int64_t tiles = (blocks + 9) / 10;
   const int64_t per = (blocks + tiles - 1) / tiles;
+  if (per <= 1) return launch_mb<BITS, 1>(p, stream);
   if (per <= 2) return launch_mb<BITS, 2>(p, stream);
   if (per <= 4) return launch_mb<BITS, 4>(p, stream);
   if (per <= 6) return launch_mb<BITS, 6>(p, stream);
@@ -115,8 +94,7 @@ hipError_t launch_qmm_mfma(const uint16_t* x, const uint32_t* w, const uint16_t*
   p.K = (int)K;
   p.out_f32 = out_f32 ? 1 : 0;
   p.tiles_m = p.tiles_n = 0;
-  if (M > 64) return bits == 4 ? launch_tile4<4>(p, stream) : launch_tile4<8>(p, stream);
-  return bits == 4 ? launch_tile3<4>(p, stream) : launch_tile3<8>(p, stream);
+  return bits == 4 ? launch_tile4<4>(p, stream) : launch_tile4<8>(p, stream);
 }
 
 }  // namespace bitmm
