@@ -42,14 +42,17 @@ bitmm_status device_check(hipStream_t) {
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+// Quantization groups along K the kernels take (each 16-byte chunk of codes lies in one).
+bool group_ok(int g) { return g == 32 || g == 64 || g == 128; }
+
 // Shared by qmv / qmm. Sets *empty when there is nothing to compute.
 bitmm_status validate_dense(const void* x, const uint32_t* w, const void* s, const void* b,
                             const void* y, int64_t M, int64_t N, int64_t K, int bits, int group,
                             bitmm_out out, bool* empty) {
   if (bits != 4 && bits != 8) return BITMM_ERR_UNSUPPORTED;
-  if (group != 64) return BITMM_ERR_UNSUPPORTED;
+  if (!group_ok(group)) return BITMM_ERR_UNSUPPORTED;
   if (out != BITMM_OUT_BF16 && out != BITMM_OUT_F32) return BITMM_ERR_UNSUPPORTED;
-  if (M < 0 || N < 0 || K < 1 || K % group != 0) return BITMM_ERR_SHAPE;
+  if (M < 0 || N < 0 || K < 1 || K % group != 0 || K % 64 != 0) return BITMM_ERR_SHAPE;
   // Index arithmetic inside the kernels is 32-bit per dimension.
   if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX) return BITMM_ERR_SHAPE;
   *empty = (M == 0 || N == 0);
@@ -93,7 +96,7 @@ bitmm_status bitmm_qmv(const void* x, const uint32_t* w, const void* scales, con
     hipError_t e = bitmm::launch_qmv(static_cast<const uint16_t*>(x), w,
                                      static_cast<const uint16_t*>(scales),
                                      static_cast<const uint16_t*>(biases), y, M, N, K, bits,
-                                     out == BITMM_OUT_F32, hs);
+                                     group_size, out == BITMM_OUT_F32, hs);
     return e == hipSuccess ? BITMM_OK : BITMM_ERR_LAUNCH;
   } catch (...) {
     return BITMM_ERR_LAUNCH;
@@ -114,8 +117,9 @@ bitmm_status bitmm_qmm(const void* x, const uint32_t* w, const void* scales, con
     const uint16_t* bs = static_cast<const uint16_t*>(biases);
     // M*B >= 8 selects the GEMM (the engine's routing rule); below it the GEMV kernel
     // streams W once for all rows.
-    hipError_t e = M < 8 ? bitmm::launch_qmv(xs, w, ss, bs, y, M, N, K, bits, out == BITMM_OUT_F32, hs)
-                         : bitmm::launch_qmm_mfma(xs, w, ss, bs, y, M, N, K, bits,
+    hipError_t e = M < 8 ? bitmm::launch_qmv(xs, w, ss, bs, y, M, N, K, bits, group_size,
+                                             out == BITMM_OUT_F32, hs)
+                         : bitmm::launch_qmm_mfma(xs, w, ss, bs, y, M, N, K, bits, group_size,
                                                   out == BITMM_OUT_F32, hs);
     return e == hipSuccess ? BITMM_OK : BITMM_ERR_LAUNCH;
   } catch (...) {
@@ -135,9 +139,9 @@ bitmm_status bitmm_gather_qmm(const void* x, const uint32_t* w, const void* scal
                               void* stream) {
   try {
     if (bits != 4 && bits != 8) return BITMM_ERR_UNSUPPORTED;
-    if (group_size != 64) return BITMM_ERR_UNSUPPORTED;
+    if (!group_ok(group_size)) return BITMM_ERR_UNSUPPORTED;
     if (out != BITMM_OUT_BF16 && out != BITMM_OUT_F32) return BITMM_ERR_UNSUPPORTED;
-    if (B < 0 || N < 0 || K < 1 || E < 1 || K % group_size != 0) return BITMM_ERR_SHAPE;
+    if (B < 0 || N < 0 || K < 1 || E < 1 || K % group_size != 0 || K % 64 != 0) return BITMM_ERR_SHAPE;
     if (B > INT32_MAX || N > INT32_MAX || K > INT32_MAX || E > INT32_MAX - 2)
       return BITMM_ERR_SHAPE;
     if (B == 0 || N == 0) return BITMM_OK;
@@ -153,7 +157,7 @@ bitmm_status bitmm_gather_qmm(const void* x, const uint32_t* w, const void* scal
     if (st != BITMM_OK) return st;
     hipError_t e = bitmm::launch_gather_qmm(
         static_cast<const uint16_t*>(x), w, static_cast<const uint16_t*>(scales),
-        static_cast<const uint16_t*>(biases), expert_idx, y, B, N, K, E, bits,
+        static_cast<const uint16_t*>(biases), expert_idx, y, B, N, K, E, bits, group_size,
         out == BITMM_OUT_F32, workspace, hs);
     return e == hipSuccess ? BITMM_OK : BITMM_ERR_LAUNCH;
   } catch (...) {
@@ -174,9 +178,9 @@ bitmm_status bitmm_gather_qmm_indexed(const void* x, const uint32_t* w, const vo
                                       void* stream) {
   try {
     if (bits != 4 && bits != 8) return BITMM_ERR_UNSUPPORTED;
-    if (group_size != 64) return BITMM_ERR_UNSUPPORTED;
+    if (!group_ok(group_size)) return BITMM_ERR_UNSUPPORTED;
     if (out != BITMM_OUT_BF16 && out != BITMM_OUT_F32) return BITMM_ERR_UNSUPPORTED;
-    if (B < 0 || N < 0 || T < 0 || K < 1 || E < 1 || K % group_size != 0) return BITMM_ERR_SHAPE;
+    if (B < 0 || N < 0 || T < 0 || K < 1 || E < 1 || K % group_size != 0 || K % 64 != 0) return BITMM_ERR_SHAPE;
     if (B > INT32_MAX || N > INT32_MAX || K > INT32_MAX || T > INT32_MAX || E > INT32_MAX - 2)
       return BITMM_ERR_SHAPE;
     // Per-expert counters live in LDS; activation offsets are 32-bit.
@@ -196,7 +200,7 @@ bitmm_status bitmm_gather_qmm_indexed(const void* x, const uint32_t* w, const vo
     hipError_t e = bitmm::launch_gather_qmm_indexed(
         static_cast<const uint16_t*>(x), w, static_cast<const uint16_t*>(scales),
         static_cast<const uint16_t*>(biases), token_idx, expert_idx, y, B, N, K, E, T, bits,
-        out == BITMM_OUT_F32, workspace, hs);
+        group_size, out == BITMM_OUT_F32, workspace, hs);
     return e == hipSuccess ? BITMM_OK : BITMM_ERR_LAUNCH;
   } catch (...) {
     return BITMM_ERR_LAUNCH;
@@ -210,9 +214,9 @@ bitmm_status bitmm_gather_qmv(const void* x, const uint32_t* w, const void* scal
                               void* stream) {
   try {
     if (bits != 4 && bits != 8) return BITMM_ERR_UNSUPPORTED;
-    if (group_size != 64) return BITMM_ERR_UNSUPPORTED;
+    if (!group_ok(group_size)) return BITMM_ERR_UNSUPPORTED;
     if (out != BITMM_OUT_BF16 && out != BITMM_OUT_F32) return BITMM_ERR_UNSUPPORTED;
-    if (B < 0 || N < 0 || T < 0 || K < 1 || E < 1 || K % group_size != 0) return BITMM_ERR_SHAPE;
+    if (B < 0 || N < 0 || T < 0 || K < 1 || E < 1 || K % group_size != 0 || K % 64 != 0) return BITMM_ERR_SHAPE;
     if (B > INT32_MAX || N > INT32_MAX || K > INT32_MAX || E > INT32_MAX || T > INT32_MAX)
       return BITMM_ERR_SHAPE;
     if (B == 0 || N == 0) return BITMM_OK;
@@ -227,7 +231,7 @@ bitmm_status bitmm_gather_qmv(const void* x, const uint32_t* w, const void* scal
     hipError_t e = bitmm::launch_gather_qmv(
         static_cast<const uint16_t*>(x), w, static_cast<const uint16_t*>(scales),
         static_cast<const uint16_t*>(biases), token_idx, expert_idx, y, B, N, K, E, T, bits,
-        out == BITMM_OUT_F32, hs);
+        group_size, out == BITMM_OUT_F32, hs);
     return e == hipSuccess ? BITMM_OK : BITMM_ERR_LAUNCH;
   } catch (...) {
     return BITMM_ERR_LAUNCH;

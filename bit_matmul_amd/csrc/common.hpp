@@ -6,7 +6,6 @@
 
 namespace bitmm {
 
-constexpr int kGroup = 64;   // quantization group along K
 constexpr int kWave = 64;    // CDNA wavefront width
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));

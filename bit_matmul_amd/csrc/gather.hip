@@ -151,6 +151,7 @@ struct GatherParams {
   const uint32_t* ws;
   const int32_t* tok;  // indexed form: token per output row (or null)
   int B, N, K, E, T;
+  int group;
   int tiles_n;
   int out_f32;
 };
@@ -193,14 +194,14 @@ __global__ __launch_bounds__(T::THREADS) void gather_qmm_kernel(GatherParams p) 
   if (r_begin >= r_end) return;
 
   const int64_t words = (int64_t)p.K * BITS / 32;
-  const int64_t groups = p.K / kGroup;
+  const int64_t groups = p.K / p.group;
   const uint32_t* we = p.w + (int64_t)e * p.N * words;
   const uint16_t* se = p.s + (int64_t)e * p.N * groups;
   const uint16_t* be = p.b + (int64_t)e * p.N * groups;
   for (int r0 = r_begin; r0 < r_end; r0 += T::BM) {
     if (r0 > r_begin) __syncthreads();  // LDS is reused by the next row block
     const int rows = min(T::BM, r_end - r0);
-    T::run(p.x + (int64_t)r0 * p.K, rows, we, se, be, n0, p.N, p.K,
+    T::run(p.x + (int64_t)r0 * p.K, rows, we, se, be, n0, p.N, p.K, p.group,
            static_cast<char*>(p.y) + (size_t)r0 * p.N * ysz, p.out_f32 != 0, lds);
   }
 }
@@ -220,14 +221,15 @@ __global__ __launch_bounds__(T::THREADS) void gather_qmm_indexed_kernel(GatherPa
   const int r_end = off[e + 1];
   if (r_begin >= r_end) return;
   const int64_t words = (int64_t)p.K * BITS / 32;
-  const int64_t groups = p.K / kGroup;
+  const int64_t groups = p.K / p.group;
   const uint32_t* we = p.w + (int64_t)e * p.N * words;
   const uint16_t* se = p.s + (int64_t)e * p.N * groups;
   const uint16_t* be = p.b + (int64_t)e * p.N * groups;
   for (int r0 = r_begin; r0 < r_end; r0 += T::BM) {
     if (r0 > r_begin) __syncthreads();  // LDS is reused by the next row block
     const int rows = min(T::BM, r_end - r0);
-    T::run(p.x, rows, we, se, be, n0, p.N, p.K, p.y, p.out_f32 != 0, lds, perm + r0, p.tok, p.T);
+    T::run(p.x, rows, we, se, be, n0, p.N, p.K, p.group, p.y, p.out_f32 != 0, lds, perm + r0, p.tok,
+           p.T);
   }
 }
 
@@ -259,7 +261,7 @@ hipError_t launch_form(GatherParams p, hipStream_t stream) {
 
 template <int BITS, int MB, bool RMAP>
 hipError_t launch_sb(GatherParams p, hipStream_t stream) {
-  const int G = p.K / kGroup;
+  const int G = p.K / p.group;  // scale values per weight row
   const bool wide = G % 2 == 0 && (reinterpret_cast<uintptr_t>(p.s) & 3) == 0 &&
                     (reinterpret_cast<uintptr_t>(p.b) & 3) == 0;
   if (G <= 12)
@@ -292,8 +294,8 @@ size_t gather_workspace_bytes(int64_t E) {
 
 hipError_t launch_gather_qmm(const uint16_t* x, const uint32_t* w, const uint16_t* scales,
                              const uint16_t* biases, const int32_t* expert_idx, void* y,
-                             int64_t B, int64_t N, int64_t K, int64_t E, int bits, bool out_f32,
-                             void* workspace, hipStream_t stream) {
+                             int64_t B, int64_t N, int64_t K, int64_t E, int bits, int group,
+                             bool out_f32, void* workspace, hipStream_t stream) {
   uint32_t* ws = static_cast<uint32_t*>(workspace);
   hipLaunchKernelGGL(gather_prepare_kernel, dim3(1), dim3(kPrepThreads), 0, stream, expert_idx,
                      (int)B, (int)E, ws);
@@ -312,6 +314,7 @@ hipError_t launch_gather_qmm(const uint16_t* x, const uint32_t* w, const uint16_
   p.K = (int)K;
   p.E = (int)E;
   p.T = (int)B;
+  p.group = group;
   p.tiles_n = 0;
   p.out_f32 = out_f32 ? 1 : 0;
   return bits == 4 ? launch_tile4<4, false>(p, stream) : launch_tile4<8, false>(p, stream);
@@ -327,8 +330,8 @@ int64_t gather_indexed_max_experts() { return kMaxIndexedExperts; }
 hipError_t launch_gather_qmm_indexed(const uint16_t* x, const uint32_t* w, const uint16_t* scales,
                                      const uint16_t* biases, const int32_t* token_idx,
                                      const int32_t* expert_idx, void* y, int64_t B, int64_t N,
-                                     int64_t K, int64_t E, int64_t T, int bits, bool out_f32,
-                                     void* workspace, hipStream_t stream) {
+                                     int64_t K, int64_t E, int64_t T, int bits, int group,
+                                     bool out_f32, void* workspace, hipStream_t stream) {
   uint32_t* ws = static_cast<uint32_t*>(workspace);
   hipLaunchKernelGGL(gather_sort_kernel, dim3(1), dim3(kPrepThreads), 0, stream, token_idx,
                      expert_idx, (int)B, (int)E, (int)T, (int)N, out_f32 ? 1 : 0, y, ws);
@@ -347,6 +350,7 @@ hipError_t launch_gather_qmm_indexed(const uint16_t* x, const uint32_t* w, const
   p.K = (int)K;
   p.E = (int)E;
   p.T = (int)T;
+  p.group = group;
   p.tiles_n = 0;
   p.out_f32 = out_f32 ? 1 : 0;
   return bits == 4 ? launch_tile4<4, true>(p, stream) : launch_tile4<8, true>(p, stream);

@@ -52,11 +52,11 @@ __device__ __forceinline__ void static_for(F&& f) {
 // SBM chooses where a wave finds the scales and biases of its 32 weight rows:
 //   0: two 2-byte loads per group and lane, into registers, PD groups ahead;
 //   1: staged once into LDS by 4-byte copies of the wave's contiguous block (the 32 rows
-//      times G groups of each array are one contiguous span), needs G even and 4-byte
-//      aligned scale and bias arrays;
+//      times GS = K/group values of each array are one contiguous span), needs 4-byte
+//      aligned blocks;
 //   2: the same with 2-byte copies (each value in a 4-byte LDS slot), any alignment.
 // A per-group load touches one cache line per weight row; the staged copies touch one
-// or two per 64 values. GMAX is the largest G the staging area holds (SBM != 0).
+// or two per 64 values. GMAX is the largest GS the staging area holds (SBM != 0).
 // RMAP: tile rows are gathered. Tile row i is output row perm[i] of y[., N], and it
 // reads activation row tok[perm[i]] of x[T, K] (row perm[i] when tok is null); without
 // RMAP, tile row i is row i of both x_rows and y_rows.
@@ -120,7 +120,7 @@ struct MmTile4 {
   __device__ static void run(const uint16_t* __restrict__ x_rows_in, int rows_in,
                              const uint32_t* __restrict__ w_in, const uint16_t* __restrict__ sc_in,
                              const uint16_t* __restrict__ bi_in, int n0_in, int N, int K,
-                             void* __restrict__ y_rows, bool out_f32, char* lds,
+                             int group, void* __restrict__ y_rows, bool out_f32, char* lds,
                              const int32_t* __restrict__ perm = nullptr,
                              const int32_t* __restrict__ tok = nullptr, int T = 0) {
     const uint16_t* x_rows = uniform_ptr(x_rows_in);
@@ -138,7 +138,12 @@ struct MmTile4 {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lc = lane & 31;
     const int lh = lane >> 5;
-    const int G = K / kGroup;
+    const int G = K / 64;       // 64-code blocks along K: one loop body each
+    const int GS = K / group;   // scale (and bias) values per weight row
+    // Group of the lane's 32 codes in block g: lane half lh covers codes 32 lh .. 32 lh + 31.
+    const int gshift = group == 32 ? 1 : (group == 64 ? 0 : -1);
+    auto gidx_uniform = [&](int g) { return gshift > 0 ? 2 * g : (gshift == 0 ? g : g >> 1); };
+    const int glane = gshift > 0 ? lh : 0;
     const int rowbytes = K * BITS / 8;
     const int col0 = n0 + wave * 32;  // first weight row of this wave
 
@@ -148,8 +153,8 @@ struct MmTile4 {
     const __amdgpu_buffer_rsrc_t rx = make_rsrc(x_rows, (int64_t)(RMAP ? T : rows) * K * 2);
     const __amdgpu_buffer_rsrc_t rw =
         make_rsrc(reinterpret_cast<const char*>(w) + (int64_t)col0 * rowbytes, (int64_t)(N - col0) * rowbytes);
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(sc + (int64_t)col0 * G, (int64_t)(N - col0) * G * 2);
-    const __amdgpu_buffer_rsrc_t rb = make_rsrc(bi + (int64_t)col0 * G, (int64_t)(N - col0) * G * 2);
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(sc + (int64_t)col0 * GS, (int64_t)(N - col0) * GS * 2);
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(bi + (int64_t)col0 * GS, (int64_t)(N - col0) * GS * 2);
     uint32_t xoff[XC];
 #pragma unroll
     for (int k = 0; k < XC; ++k) {
@@ -168,7 +173,7 @@ struct MmTile4 {
       }
     }
     const uint32_t woff = (uint32_t)(lc * rowbytes + lh * 16 * WV);
-    const uint32_t soff = (uint32_t)(lc * G * 2);
+    const uint32_t soff = (uint32_t)((lc * GS + glane) * 2);
     // Activation read offsets within a buffer for k-step u (row lc of row block 0).
     int aoff[4];
 #pragma unroll
@@ -183,14 +188,14 @@ struct MmTile4 {
         r.q[v] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
                                                  rw, woff + v * 16, gc * GB, 0));
       if constexpr (SBM == 0) {
-        r.s = __builtin_amdgcn_raw_buffer_load_b16(rs, soff, gc * 2, 0);
-        r.b = __builtin_amdgcn_raw_buffer_load_b16(rb, soff, gc * 2, 0);
+        r.s = __builtin_amdgcn_raw_buffer_load_b16(rs, soff, gidx_uniform(gc) * 2, 0);
+        r.b = __builtin_amdgcn_raw_buffer_load_b16(rb, soff, gidx_uniform(gc) * 2, 0);
       }
     };
     // Staged scales and biases: this wave's region, value of row lc and group g.
     char* const sbw = lds + NB * XB + wave * 2 * SB_ARR;
     auto sb_read = [&](int g, uint32_t& sv, uint32_t& bv) {
-      const int o = (lc * G + min(g, G - 1)) * SB_EL;
+      const int o = (lc * GS + gidx_uniform(min(g, G - 1)) + glane) * SB_EL;
       sv = *reinterpret_cast<const uint16_t*>(sbw + o);
       bv = *reinterpret_cast<const uint16_t*>(sbw + SB_ARR + o);
     };
@@ -278,7 +283,7 @@ struct MmTile4 {
     if constexpr (SBM != 0) {
       // Lane L of copy j carries values 64 j + L (2-byte form) or 128 j + 2 L, +1 (4-byte
       // form) of the wave's block; rows past N read as zeros.
-      const int ncopy = (32 * G * SB_EL + 255) / 256;
+      const int ncopy = (32 * GS * SB_EL + 255) / 256;
       for (int j = 0; j < ncopy; ++j) {
         const uint32_t vo = (uint32_t)((j * 64 + lane) * (SBM == 1 ? 4 : 2));
         if constexpr (SBM == 1) {

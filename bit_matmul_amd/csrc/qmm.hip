@@ -14,6 +14,7 @@ struct QmmParams {
   const uint16_t* b;
   void* y;
   int M, N, K;
+  int group;
   int tiles_m, tiles_n;
   int out_f32;
 };
@@ -37,7 +38,7 @@ __global__ __launch_bounds__(T::THREADS) void qmm_mfma_kernel(QmmParams p) {
   const int m0 = tm * T::BM;
   const int rows = min(T::BM, p.M - m0);
   const size_t ysz = p.out_f32 ? 4 : 2;
-  T::run(p.x + (int64_t)m0 * p.K, rows, p.w, p.s, p.b, tn * T::BN, p.N, p.K,
+  T::run(p.x + (int64_t)m0 * p.K, rows, p.w, p.s, p.b, tn * T::BN, p.N, p.K, p.group,
          static_cast<char*>(p.y) + (size_t)m0 * p.N * ysz, p.out_f32 != 0, lds);
 }
 
@@ -58,7 +59,7 @@ hipError_t launch_tiles(QmmParams p, hipStream_t stream) {
 // 92 us. At 320 rows the activation buffers and the staging area fill the 160 KB.
 template <int BITS, int MB>
 hipError_t launch_mb(QmmParams p, hipStream_t stream) {
-  const int G = p.K / kGroup;
+  const int G = p.K / p.group;  // scale values per weight row
   const bool stage = G <= 80 && G % 2 == 0 && (reinterpret_cast<uintptr_t>(p.s) & 3) == 0 &&
                      (reinterpret_cast<uintptr_t>(p.b) & 3) == 0;
   return stage ? launch_tiles<MmTile4<BITS, MB, 4, 3, 2, 1, 80>>(p, stream)
@@ -82,7 +83,7 @@ hipError_t launch_tile4(QmmParams p, hipStream_t stream) {
 
 hipError_t launch_qmm_mfma(const uint16_t* x, const uint32_t* w, const uint16_t* scales,
                            const uint16_t* biases, void* y, int64_t M, int64_t N, int64_t K,
-                           int bits, bool out_f32, hipStream_t stream) {
+                           int bits, int group, bool out_f32, hipStream_t stream) {
   QmmParams p;
   p.x = x;
   p.w = w;
@@ -92,6 +93,7 @@ hipError_t launch_qmm_mfma(const uint16_t* x, const uint32_t* w, const uint16_t*
   p.M = (int)M;
   p.N = (int)N;
   p.K = (int)K;
+  p.group = group;
   p.out_f32 = out_f32 ? 1 : 0;
   p.tiles_m = p.tiles_n = 0;
   return bits == 4 ? launch_tile4<4>(p, stream) : launch_tile4<8>(p, stream);

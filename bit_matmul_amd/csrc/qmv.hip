@@ -56,7 +56,7 @@ namespace {
 // of `bt` with one activation row each (M = 1).
 hipError_t launch_rows(const uint16_t* x, const uint32_t* w, const uint16_t* scales,
                        const uint16_t* biases, void* y, int64_t M, int64_t N, int64_t K, int bits,
-                       bool out_f32, const GemvBatch& bt, hipStream_t stream) {
+                       int group, bool out_f32, const GemvBatch& bt, hipStream_t stream) {
   const int64_t nch = K * bits / 128;  // 16-byte code chunks per weight row
   const size_t ysz = out_f32 ? 4 : 2;
   if (M == 1 && forced_path() == 0 && qmv_dma_detail::pick_lanes(nch) != 0) {
@@ -68,6 +68,7 @@ hipError_t launch_rows(const uint16_t* x, const uint32_t* w, const uint16_t* sca
     dp.y = y;
     dp.N = (int)N;
     dp.K = (int)K;
+    dp.group = group;
     dp.out_f32 = out_f32 ? 1 : 0;
     dp.steps_per_wave = dp.total_steps = 0;
     dp.bt = bt;
@@ -85,6 +86,7 @@ hipError_t launch_rows(const uint16_t* x, const uint32_t* w, const uint16_t* sca
     sp.y = y;
     sp.N = (int)N;
     sp.K = (int)K;
+    sp.group = group;
     sp.out_f32 = out_f32 ? 1 : 0;
     sp.bt = bt;
     return bits == 4 ? qmv_split_detail::launch_bits<4>(sp, (int)M, stream)
@@ -105,6 +107,7 @@ hipError_t launch_rows(const uint16_t* x, const uint32_t* w, const uint16_t* sca
     p.y = static_cast<char*>(y) + (size_t)(m0 * N) * ysz;
     p.N = (int)N;
     p.K = (int)K;
+    p.group = group;
     p.out_f32 = out_f32 ? 1 : 0;
     p.bt = bt;
     const hipError_t e = bits == 4 ? qmv_detail::launch_bits<4>(p, mr, cpl, stream)
@@ -118,15 +121,16 @@ hipError_t launch_rows(const uint16_t* x, const uint32_t* w, const uint16_t* sca
 
 hipError_t launch_qmv(const uint16_t* x, const uint32_t* w, const uint16_t* scales,
                       const uint16_t* biases, void* y, int64_t M, int64_t N, int64_t K, int bits,
-                      bool out_f32, hipStream_t stream) {
+                      int group, bool out_f32, hipStream_t stream) {
   GemvBatch none{};
-  return launch_rows(x, w, scales, biases, y, M, N, K, bits, out_f32, none, stream);
+  return launch_rows(x, w, scales, biases, y, M, N, K, bits, group, out_f32, none, stream);
 }
 
 hipError_t launch_gather_qmv(const uint16_t* x, const uint32_t* w, const uint16_t* scales,
                              const uint16_t* biases, const int32_t* token_idx,
                              const int32_t* expert_idx, void* y, int64_t B, int64_t N, int64_t K,
-                             int64_t E, int64_t T, int bits, bool out_f32, hipStream_t stream) {
+                             int64_t E, int64_t T, int bits, int group, bool out_f32,
+                             hipStream_t stream) {
   constexpr int64_t kMaxGridRows = 65535;  // one launch per this many output rows
   GemvBatch bt;
   bt.tok = token_idx;
@@ -134,11 +138,11 @@ hipError_t launch_gather_qmv(const uint16_t* x, const uint32_t* w, const uint16_
   bt.T = (int)T;
   bt.E = (int)E;
   bt.w_stride = N * K * bits / 32;
-  bt.sb_stride = N * (K / 64);
+  bt.sb_stride = N * (K / group);
   for (int64_t r0 = 0; r0 < B; r0 += kMaxGridRows) {
     bt.row0 = (int)r0;
     bt.rows = (int)(B - r0 < kMaxGridRows ? B - r0 : kMaxGridRows);
-    const hipError_t e = launch_rows(x, w, scales, biases, y, 1, N, K, bits, out_f32, bt, stream);
+    const hipError_t e = launch_rows(x, w, scales, biases, y, 1, N, K, bits, group, out_f32, bt, stream);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

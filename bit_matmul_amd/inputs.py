@@ -123,14 +123,14 @@ def bias_for_scales(scale_bits: np.ndarray, bits: int) -> np.ndarray:
 class Dense:
     """One qmv / qmm problem: y[M,N] = x[M,K] . dequant(w)^T."""
 
-    def __init__(self, name, x, w, scales, biases, bits):
+    def __init__(self, name, x, w, scales, biases, bits, group: int = GROUP):
         self.name = name
         self.x, self.w, self.scales, self.biases = x, w, scales, biases
-        self.bits = bits
+        self.bits, self.group = bits, group
         self.M, self.K = x.shape
         self.N = w.shape[0]
         assert w.shape == (self.N, self.K * bits // 32)
-        assert scales.shape == biases.shape == (self.N, self.K // GROUP)
+        assert scales.shape == biases.shape == (self.N, self.K // group)
 
     def algorithmic_bytes(self, out_bytes: int = 2) -> int:
         """Codes + scales + biases + x + y, each moved once."""
@@ -144,16 +144,17 @@ class Dense:
 class Gather:
     """One expert-sorted problem: y[r,:] = x[r,:] . dequant(w[expert_idx[r]])^T."""
 
-    def __init__(self, name, x, w, scales, biases, expert_idx, bits, token_of_row=None):
+    def __init__(self, name, x, w, scales, biases, expert_idx, bits, token_of_row=None,
+                 group: int = GROUP):
         self.name = name
         self.x, self.w, self.scales, self.biases = x, w, scales, biases
         self.expert_idx = expert_idx
         self.token_of_row = token_of_row
-        self.bits = bits
+        self.bits, self.group = bits, group
         self.B, self.K = x.shape
         self.E, self.N = w.shape[0], w.shape[1]
         assert w.shape == (self.E, self.N, self.K * bits // 32)
-        assert scales.shape == biases.shape == (self.E, self.N, self.K // GROUP)
+        assert scales.shape == biases.shape == (self.E, self.N, self.K // group)
         assert expert_idx.shape == (self.B,) and expert_idx.dtype == np.int32
 
     def algorithmic_bytes(self, out_bytes: int = 2) -> int:
@@ -168,16 +169,16 @@ class GatherIndexed:
     """Indexed gather: y[r,:] = x[token_idx[r],:] . dequant(w[expert_idx[r]])^T, rows in
     any order (token_idx None: row r reads x row r)."""
 
-    def __init__(self, name, x, w, scales, biases, token_idx, expert_idx, bits):
+    def __init__(self, name, x, w, scales, biases, token_idx, expert_idx, bits, group: int = GROUP):
         self.name = name
         self.x, self.w, self.scales, self.biases = x, w, scales, biases
         self.token_idx, self.expert_idx = token_idx, expert_idx
-        self.bits = bits
+        self.bits, self.group = bits, group
         self.T, self.K = x.shape
         self.E, self.N = w.shape[0], w.shape[1]
         self.B = expert_idx.shape[0]
         assert w.shape == (self.E, self.N, self.K * bits // 32)
-        assert scales.shape == biases.shape == (self.E, self.N, self.K // GROUP)
+        assert scales.shape == biases.shape == (self.E, self.N, self.K // group)
         assert expert_idx.dtype == np.int32
         assert token_idx is None or (token_idx.shape == (self.B,) and token_idx.dtype == np.int32)
 
@@ -194,9 +195,9 @@ class GatherIndexed:
         return 2 * self.B * self.N * self.K
 
 
-def _dense_weights(seed: int, N: int, K: int, bits: int, sub: int = 0):
+def _dense_weights(seed: int, N: int, K: int, bits: int, sub: int = 0, group: int = GROUP):
     w = random_words(rng_for(seed, TAG_Q, bits, N, K, sub), (N, K * bits // 32))
-    s = random_scales(rng_for(seed, TAG_SCALE, N, K, sub), (N, K // GROUP))
+    s = random_scales(rng_for(seed, TAG_SCALE, N, K, sub), (N, K // group))
     return w, s, bias_for_scales(s, bits)
 
 
@@ -335,7 +336,7 @@ def moe_decode(which: str, tokens: int = 1, seed: int = 0, E: int = MOE_E, top_k
 
 
 def random_indexed(T: int, B: int, E: int, N: int, K: int, bits: int, seed: int = 0,
-                   with_tokens: bool = True) -> GatherIndexed:
+                   with_tokens: bool = True, group: int = GROUP) -> GatherIndexed:
     """Arbitrary indexed gather: random token and expert per row (repeats, any order)."""
     rng = rng_for(seed, TAG_ROUTE, 9, T, B, E, N, K)
     exp = rng.integers(0, E, B).astype(np.int32)
@@ -343,20 +344,22 @@ def random_indexed(T: int, B: int, E: int, N: int, K: int, bits: int, seed: int 
     rows = T if with_tokens else B
     x = to_bf16_bits(rng_for(seed, TAG_X, 9, rows, K).standard_normal(size=(rows, K)))
     w = random_words(rng_for(seed, TAG_Q, bits, E, N, K, 9), (E, N, K * bits // 32))
-    s = random_scales(rng_for(seed, TAG_SCALE, E, N, K, 9), (E, N, K // GROUP))
+    s = random_scales(rng_for(seed, TAG_SCALE, E, N, K, 9), (E, N, K // group))
     b = bias_for_scales(s, bits)
-    return GatherIndexed(f"indexed_T{rows}_B{B}_E{E}_K{K}_N{N}_b{bits}", x, w, s, b, tok, exp, bits)
+    return GatherIndexed(f"indexed_T{rows}_B{B}_E{E}_K{K}_N{N}_b{bits}", x, w, s, b, tok, exp, bits,
+                         group)
 
 
-def random_dense(M: int, N: int, K: int, bits: int, seed: int = 0, x_dist: str = "normal") -> Dense:
+def random_dense(M: int, N: int, K: int, bits: int, seed: int = 0, x_dist: str = "normal",
+                 group: int = GROUP) -> Dense:
     """Arbitrary-shape dense problem with the standard value distributions."""
     rx = rng_for(seed, TAG_X, 7, M, N, K)
     xf = rx.standard_normal(size=(M, K)) if x_dist == "normal" else rx.uniform(-1, 1, size=(M, K))
-    w, s, b = _dense_weights(seed, N, K, bits, sub=7)
-    return Dense(f"dense_M{M}_K{K}_N{N}_b{bits}", to_bf16_bits(xf), w, s, b, bits)
+    w, s, b = _dense_weights(seed, N, K, bits, sub=7, group=group)
+    return Dense(f"dense_M{M}_K{K}_N{N}_b{bits}", to_bf16_bits(xf), w, s, b, bits, group)
 
 
-def random_gather(counts, N: int, K: int, bits: int, seed: int = 0) -> Gather:
+def random_gather(counts, N: int, K: int, bits: int, seed: int = 0, group: int = GROUP) -> Gather:
     """Expert-sorted problem with explicit per-expert row counts (zeros allowed)."""
     counts = np.asarray(counts, dtype=np.int64)
     E = counts.shape[0]
@@ -364,6 +367,6 @@ def random_gather(counts, N: int, K: int, bits: int, seed: int = 0) -> Gather:
     B = idx.shape[0]
     x = to_bf16_bits(rng_for(seed, TAG_X, 8, B, N, K).standard_normal(size=(B, K)))
     w = random_words(rng_for(seed, TAG_Q, bits, E, N, K, 8), (E, N, K * bits // 32))
-    s = random_scales(rng_for(seed, TAG_SCALE, E, N, K, 8), (E, N, K // GROUP))
+    s = random_scales(rng_for(seed, TAG_SCALE, E, N, K, 8), (E, N, K // group))
     b = bias_for_scales(s, bits)
-    return Gather(f"gather_B{B}_E{E}_K{K}_N{N}_b{bits}", x, w, s, b, idx, bits)
+    return Gather(f"gather_B{B}_E{E}_K{K}_N{N}_b{bits}", x, w, s, b, idx, bits, group=group)

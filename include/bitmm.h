@@ -13,7 +13,7 @@
  * three compute
  *
  *     y[r][n] = sum_k x[r][k] * w[e_r][n][k],
- *     w[e][n][k] = s[e][n][k/64] * q[e][n][k] + b[e][n][k/64],
+ *     w[e][n][k] = s[e][n][k/gs] * q[e][n][k] + b[e][n][k/gs],   gs = group_size,
  *
  * with e_r = 0 for the dense forms and e_r = expert_idx[r] for the gathered one.
  *
@@ -22,8 +22,8 @@
  *   w        uint32 [E, N, K*bits/32]    (codes along K, LSB first: code j of a word
  *                                         sits in bits [bits*j, bits*(j+1)) and word i
  *                                         of a row holds k = i*(32/bits) + j)
- *   scales   bf16 [E, N, K/64]           (one scale per row n and group of 64 along K)
- *   biases   bf16 [E, N, K/64]
+ *   scales   bf16 [E, N, K/group_size]   (one scale per row n and group along K)
+ *   biases   bf16 [E, N, K/group_size]
  *   y        bf16 or f32 [M, N]          (bf16 rounded to nearest even from f32)
  * Dense calls have E = 1 and no leading E dimension.
  *
@@ -61,8 +61,10 @@ extern "C" {
 typedef enum {
   BITMM_OK = 0,
   BITMM_ERR_NULL = 1,        /* a required pointer is NULL                                  */
-  BITMM_ERR_SHAPE = 2,       /* M, N, B < 0; K < 1; E < 1; or K % group_size != 0           */
-  BITMM_ERR_UNSUPPORTED = 3, /* bits not in {4, 8}; group_size != 64; unknown output type   */
+  BITMM_ERR_SHAPE = 2,       /* M, N, B < 0; K < 1; E < 1; K not a multiple of 64 and of
+                                group_size                                                  */
+  BITMM_ERR_UNSUPPORTED = 3, /* bits not in {4, 8}; group_size not in {32, 64, 128}; unknown
+                                output type                                                 */
   BITMM_ERR_ALIGN = 4,       /* x, w or workspace not 16-byte aligned; scales or biases not
                                 2-byte aligned; y not aligned to its element size;
                                 expert_idx not 4-byte aligned                               */
@@ -84,7 +86,10 @@ const char* bitmm_status_string(bitmm_status s);
  * rows (rows are taken eight at a time). Meant for M = 1 (the decode step the epic's
  * kernel table lists second); any M >= 0 is accepted.
  *   x: bf16 [M, K]; w: uint32 [N, K*bits/32]; scales, biases: bf16 [N, K/group_size];
- *   y: [M, N] of type `out`. bits in {4, 8}; group_size == 64; K a multiple of 64.
+ *   y: [M, N] of type `out`. bits in {4, 8}; group_size in {32, 64, 128} (the epic's
+ *   checkpoint is group 64; its diagnosis item 4 quotes a tile rule keyed on
+ *   group_size <= 64, so other group sizes exist in the format); K a multiple of 64 and
+ *   of group_size.
  */
 bitmm_status bitmm_qmv(const void* x, const uint32_t* w, const void* scales, const void* biases,
                        void* y, int64_t M, int64_t N, int64_t K, int bits, int group_size,

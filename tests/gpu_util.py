@@ -61,7 +61,7 @@ def run_dense(fn_name, d, out="bf16", stream=None):
     t = torch()
     x, w, s, b = dense_to_dev(d)
     y = t.empty((d.M, d.N), dtype=t.bfloat16 if out == "bf16" else t.float32, device=dev())
-    getattr(bm, fn_name)(x, w, s, b, y, d.bits, stream=stream)
+    getattr(bm, fn_name)(x, w, s, b, y, d.bits, group_size=getattr(d, "group", 64), stream=stream)
     return y
 
 
@@ -70,7 +70,7 @@ def run_gather(g, out="bf16", idx=None):
     x, w, s, b, e = gather_to_dev(g, idx)
     y = t.empty((g.B, g.N), dtype=t.bfloat16 if out == "bf16" else t.float32, device=dev())
     ws = t.empty(bm.bitmm_gather_qmm_workspace_bytes(g.B, g.N, g.E), dtype=t.uint8, device=dev())
-    bm.bitmm_gather_qmm(x, w, s, b, e, y, ws, g.bits)
+    bm.bitmm_gather_qmm(x, w, s, b, e, y, ws, g.bits, group_size=getattr(g, "group", 64))
     return y, ws
 
 

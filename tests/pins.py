@@ -153,6 +153,25 @@ def check_brute_force(O):
                     assert err <= 1e-12 * max(1.0, np.max(np.abs(ref))), (bits, M, N, K, err)
 
 
+def check_brute_force_groups(O):
+    """Groups of 32 and 128 along K: oracle == numpy (byte-view unpack, scales and
+    biases repeated over their group, float64 matmul), dense and indexed gather."""
+    for group in (32, 128):
+        for bits in (4, 8):
+            for M, N, K in ((1, 5, 128), (3, 8, 256), (2, 17, 384)):
+                d = I.random_dense(M, N, K, bits, seed=M * 100 + N + K + group, group=group)
+                ref = numpy_qmm(d.x, d.w, d.scales, d.biases, bits, group)
+                got = O.qmm(d.x, d.w, d.scales, d.biases, bits, group=group)
+                assert np.allclose(got, ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max()), (group, bits, M, N, K)
+            g = I.random_indexed(3, 9, 4, 7, 256, bits, seed=group + bits, group=group)
+            got = O.gather_qmm_indexed(g.x, g.w, g.scales, g.biases, g.token_idx, g.expert_idx,
+                                       bits, group=group)
+            xf = I.bf16_bits_to_f64(g.x)
+            ref = np.stack([numpy_dequant(g.w[e], g.scales[e], g.biases[e], bits, group) @ xf[t]
+                            for t, e in zip(g.token_idx, g.expert_idx)])
+            assert np.allclose(got, ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max()), (group, bits)
+
+
 def integer_exact_problem(M, N, K, bits, seed):
     """x in {-2..2}, s in {1/4,1/2,1,2} per group, b = -2**(bits-1)*s: every
     weight, product and partial sum is an exact multiple of 1/4 below 2**24/4."""
@@ -377,6 +396,7 @@ ALL_CHECKS = [
     check_unpack_golden,
     check_weight_definition,
     check_brute_force,
+    check_brute_force_groups,
     check_integer_exact,
     check_one_hot,
     check_closed_form,

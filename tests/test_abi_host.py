@@ -84,10 +84,13 @@ def dense_args(**kw):
 DENSE_CASES = [
     (dict(bits=3), bm.BITMM_ERR_UNSUPPORTED),
     (dict(bits=2), bm.BITMM_ERR_UNSUPPORTED),
-    (dict(group=32), bm.BITMM_ERR_UNSUPPORTED),
-    (dict(group=128), bm.BITMM_ERR_UNSUPPORTED),
+    (dict(group=16), bm.BITMM_ERR_UNSUPPORTED),
+    (dict(group=256), bm.BITMM_ERR_UNSUPPORTED),
+    (dict(group=48), bm.BITMM_ERR_UNSUPPORTED),
     (dict(out=2), bm.BITMM_ERR_UNSUPPORTED),
     (dict(K=100), bm.BITMM_ERR_SHAPE),
+    (dict(K=96, group=32), bm.BITMM_ERR_SHAPE),    # K must also be a multiple of 64
+    (dict(K=576, group=128), bm.BITMM_ERR_SHAPE),  # and of the group size
     (dict(K=0), bm.BITMM_ERR_SHAPE),
     (dict(K=-64), bm.BITMM_ERR_SHAPE),
     (dict(M=-1), bm.BITMM_ERR_SHAPE),
@@ -128,7 +131,8 @@ def test_dense_valid_without_device(L):
     for fn in (L.bitmm_qmv, L.bitmm_qmm):
         for bits in (4, 8):
             for M in (1, 3, 8, 600):
-                assert fn(*dense_args(bits=bits, M=M, out=1)) == bm.BITMM_ERR_DEVICE
+                for group in (32, 64, 128):
+                    assert fn(*dense_args(bits=bits, M=M, out=1, group=group)) == bm.BITMM_ERR_DEVICE
 
 
 def gather_args(**kw):
@@ -183,8 +187,9 @@ def gqmv_args(**kw):
 
 GQMV_CASES = [
     (dict(bits=2), bm.BITMM_ERR_UNSUPPORTED),
-    (dict(group=128), bm.BITMM_ERR_UNSUPPORTED),
+    (dict(group=256), bm.BITMM_ERR_UNSUPPORTED),
     (dict(out=7), bm.BITMM_ERR_UNSUPPORTED),
+    (dict(K=704, group=128), bm.BITMM_ERR_SHAPE),
     (dict(E=0), bm.BITMM_ERR_SHAPE),
     (dict(K=0), bm.BITMM_ERR_SHAPE),
     (dict(K=96), bm.BITMM_ERR_SHAPE),
@@ -231,7 +236,7 @@ def gidx_args(**kw):
 
 GIDX_CASES = [
     (dict(bits=3), bm.BITMM_ERR_UNSUPPORTED),
-    (dict(group=32), bm.BITMM_ERR_UNSUPPORTED),
+    (dict(group=16), bm.BITMM_ERR_UNSUPPORTED),
     (dict(out=2), bm.BITMM_ERR_UNSUPPORTED),
     (dict(E=8193), bm.BITMM_ERR_UNSUPPORTED),
     (dict(T=1 << 20, K=1024), bm.BITMM_ERR_UNSUPPORTED),
