@@ -1,5 +1,8 @@
 """Python access to the CPU oracle (``oracle.c``): test infrastructure only.
 
+It covers the affine group-wise quantized products (qmm, gather_qmm and the indexed
+gather) and the dense grouped product gather_mm.
+
 Only the tests, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
 ``bench.py`` use this package. The library under ``bit_matmul_amd`` never
 imports it, and it never imports the library.
@@ -69,6 +72,19 @@ class Oracle:
         lib.oracle_gather_qmm_indexed_points.argtypes = [P, P, P, P, P, P, I64, I64, I64, I64,
                                                          I64, I, I, P, P, I64, P, I]
         lib.oracle_gather_qmm_indexed_points.restype = I
+        lib.oracle_f16_to_f64.argtypes = [ctypes.c_uint16]
+        lib.oracle_f16_to_f64.restype = ctypes.c_double
+        lib.oracle_f64_to_f16_rne.argtypes = [ctypes.c_double]
+        lib.oracle_f64_to_f16_rne.restype = ctypes.c_uint16
+        lib.oracle_f64_to_f16_array.argtypes = [P, P, I64]
+        lib.oracle_f64_to_f16_array.restype = None
+        lib.oracle_f16_to_f64_array.argtypes = [P, P, I64]
+        lib.oracle_f16_to_f64_array.restype = None
+        lib.oracle_gather_mm.argtypes = [P, P, P, P, I64, I64, I64, I64, I64, I, I, P, I]
+        lib.oracle_gather_mm.restype = I
+        lib.oracle_gather_mm_points.argtypes = [P, P, P, P, I64, I64, I64, I64, I64, I, I, P, P,
+                                                I64, P, I]
+        lib.oracle_gather_mm_points.restype = I
         self.lib = lib
         self.path = path
 
@@ -84,6 +100,60 @@ class Oracle:
         out = np.empty(v.shape, dtype=np.uint16)
         self.lib.oracle_f64_to_bf16_array(pv, out.ctypes.data_as(ctypes.c_void_p), v.size)
         return out
+
+    def f16_to_f64(self, h) -> np.ndarray:
+        """Widen binary16 bit patterns to float64 (exact)."""
+        h, ph = _c(h, np.uint16)
+        out = np.empty(h.shape, dtype=np.float64)
+        self.lib.oracle_f16_to_f64_array(ph, out.ctypes.data_as(ctypes.c_void_p), h.size)
+        return out
+
+    def f64_to_f16(self, v) -> np.ndarray:
+        """Round doubles to binary16 bit patterns (nearest, ties to even)."""
+        v, pv = _c(v, np.float64)
+        out = np.empty(v.shape, dtype=np.uint16)
+        self.lib.oracle_f64_to_f16_array(pv, out.ctypes.data_as(ctypes.c_void_p), v.size)
+        return out
+
+    def gather_mm(self, x, w, token_idx, expert_idx, dtype: str = "bf16", layout: str = "nk",
+                  threads: int = 0, rows=None, cols=None) -> np.ndarray:
+        """Dense grouped product, y[B,N] (float64) or y at the points (rows[i], cols[i]):
+        row r reads x row token_idx[r] (row r when token_idx is None) and the weights of
+        expert expert_idx[r]; w is [E, N, K] (layout "nk") or [E, K, N] ("kn"); x and w
+        are bf16 or binary16 ("f16") bit patterns."""
+        x, px = _c(x, np.uint16)
+        w, pw = _c(w, np.uint16)
+        e, pe = _c(expert_idx, np.int32)
+        dt = {"bf16": 0, "f16": 1}[dtype]
+        lay = {"nk": 0, "kn": 1}[layout]
+        T, K = x.shape
+        E = w.shape[0]
+        N = w.shape[1] if lay == 0 else w.shape[2]
+        B = e.shape[0]
+        if w.shape != ((E, N, K) if lay == 0 else (E, K, N)) or e.ndim != 1:
+            raise ValueError("oracle.gather_mm: inconsistent shapes")
+        if token_idx is None:
+            pt = None
+            if T != B:
+                raise ValueError("oracle.gather_mm: x rows must equal B without token_idx")
+        else:
+            t, pt = _c(token_idx, np.int32)
+            if t.shape != (B,):
+                raise ValueError("oracle.gather_mm: token_idx shape")
+        if rows is None:
+            y = np.empty((B, N), dtype=np.float64)
+            _check(self.lib.oracle_gather_mm(px, pw, pt, pe, B, N, K, E, T, dt, lay,
+                                             y.ctypes.data_as(ctypes.c_void_p), int(threads)))
+            return y
+        r, pr = _c(rows, np.int64)
+        c, pc = _c(cols, np.int64)
+        if r.shape != c.shape:
+            raise ValueError("oracle.gather_mm: rows and cols differ in shape")
+        y = np.empty(r.shape, dtype=np.float64)
+        _check(self.lib.oracle_gather_mm_points(px, pw, pt, pe, B, N, K, E, T, dt, lay, pr, pc,
+                                                r.size, y.ctypes.data_as(ctypes.c_void_p),
+                                                int(threads)))
+        return y
 
     def code(self, row_words, k: int, bits: int) -> int:
         w, pw = _c(row_words, np.uint32)
@@ -248,6 +318,19 @@ def f64_to_bf16(v):
 
 def code(row_words, k, bits):
     return get().code(row_words, k, bits)
+
+
+def f16_to_f64(h):
+    return get().f16_to_f64(h)
+
+
+def f64_to_f16(v):
+    return get().f64_to_f16(v)
+
+
+def gather_mm(x, w, token_idx, expert_idx, dtype="bf16", layout="nk", threads=0, rows=None,
+              cols=None):
+    return get().gather_mm(x, w, token_idx, expert_idx, dtype, layout, threads, rows, cols)
 
 
 def weight(row_words, row_scales, row_biases, k, bits, group=64):

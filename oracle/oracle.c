@@ -1,5 +1,6 @@
 /*
- * CPU oracle for the affine group-wise quantized matmul. TEST INFRASTRUCTURE
+ * CPU oracle for the affine group-wise quantized matmul and the dense grouped
+ * product beside it (gather_mm). TEST INFRASTRUCTURE
  * ONLY: the tests, the smoke check and the benchmark's CPU-baseline leg use it.
  * The library never calls, links or loads it, and it shares no code with the
  * HIP kernels.
@@ -36,6 +37,17 @@
  * is given) and the weights of expert expert_idx[r], in any order. A row whose
  * token or expert id is out of range is a zero row.
  *
+ * The dense grouped product (gather_mm) is the same scheduler without the
+ * dequantization step (PR #1562: non-quantized MoE checkpoints reach the grouped
+ * GEMM through SwitchLinear::Regular::forward, and its new tests compare gather_mm
+ * with an f64 dense per-expert product in both operand layouts, in f32, bf16 and
+ * f16): row r of the output is
+ *
+ *   y[r][n] = sum_k x[t_r][k] * W[e_r][n][k]      (weights stored [E, N, K])
+ *   y[r][n] = sum_k x[t_r][k] * W[e_r][k][n]      (weights stored [E, K, N])
+ *
+ * with x and W both bf16 or both IEEE binary16, widened exactly.
+ *
  * Each output is summed sequentially in k order, and threads only split the
  * set of outputs, so results are bitwise identical for any thread count.
  *
@@ -59,6 +71,50 @@ double oracle_bf16_to_f64(uint16_t h) {
   float f;
   memcpy(&f, &u, sizeof f);
   return (double)f;
+}
+
+/* IEEE 754 binary16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits.
+ * Exponent field 0 holds zero and the subnormals f * 2^-24; field 31 holds the
+ * infinities (f = 0) and NaNs. Widening to double is exact. */
+double oracle_f16_to_f64(uint16_t h) {
+  int sign = h >> 15;
+  int field = (h >> 10) & 0x1F;
+  int frac = h & 0x3FF;
+  double v;
+  if (field == 0)
+    v = ldexp((double)frac, -24);
+  else if (field == 31)
+    v = frac ? NAN : INFINITY;
+  else
+    v = ldexp((double)(1024 + frac), field - 25);
+  return sign ? -v : v;
+}
+
+/* Round a double to the nearest binary16, ties to even, in one step: the same
+ * construction as the bf16 rounding below with a 10-bit fraction, exponent bias
+ * 15 and subnormal step 2^-24. */
+uint16_t oracle_f64_to_f16_rne(double v) {
+  uint16_t sign = signbit(v) ? 0x8000u : 0u;
+  double a = fabs(v);
+  if (isnan(v)) return (uint16_t)(sign | 0x7E00u);
+  if (isinf(v)) return (uint16_t)(sign | 0x7C00u);
+  if (a == 0.0) return sign;
+  int e;
+  frexp(a, &e); /* a = m * 2^e, m in [0.5, 1) */
+  if (e - 1 < -14) {
+    /* subnormal: value = r * 2^-24, r in [0, 1024]; r == 1024 is the smallest
+     * normal, whose encoding is also 1024. */
+    double r = nearbyint(ldexp(a, 24));
+    return (uint16_t)(sign | (uint16_t)r);
+  }
+  double r = nearbyint(ldexp(a, 11 - e)); /* in [1024, 2048] */
+  if (r == 2048.0) {
+    r = 1024.0;
+    e += 1;
+  }
+  int biased = e - 1 + 15;
+  if (biased >= 31) return (uint16_t)(sign | 0x7C00u);
+  return (uint16_t)(sign | (uint16_t)(biased << 10) | (uint16_t)((int)r - 1024));
 }
 
 /* Round a double to the nearest bf16, ties to even, in one step (no detour
@@ -282,4 +338,116 @@ int oracle_gather_qmm_indexed_points(const uint16_t* x, const uint32_t* w, const
 
 void oracle_f64_to_bf16_array(const double* v, uint16_t* out, int64_t n) {
   for (int64_t i = 0; i < n; ++i) out[i] = oracle_f64_to_bf16_rne(v[i]);
+}
+
+void oracle_f64_to_f16_array(const double* v, uint16_t* out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = oracle_f64_to_f16_rne(v[i]);
+}
+
+void oracle_f16_to_f64_array(const uint16_t* h, double* out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = oracle_f16_to_f64(h[i]);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Dense grouped product (gather_mm).                                        */
+
+typedef struct {
+  const uint16_t* x;
+  const uint16_t* w;
+  const int32_t* token_idx; /* NULL: output row r reads activation row r */
+  const int32_t* expert_idx;
+  int64_t N, K, E, T;
+  int dtype;  /* 0: bf16, 1: binary16 */
+  int layout; /* 0: W[e] is [N, K]; 1: W[e] is [K, N] */
+  const int64_t* pt_r;
+  const int64_t* pt_n;
+  int64_t count;
+  double* y;
+} dense_problem_t;
+
+static double operand(uint16_t h, int dtype) {
+  return dtype == 0 ? oracle_bf16_to_f64(h) : oracle_f16_to_f64(h);
+}
+
+static double dense_point(const dense_problem_t* p, int64_t r, int64_t n) {
+  int64_t e = p->expert_idx[r];
+  if (e < 0 || p->E <= e) return 0.0;
+  int64_t t = r;
+  if (p->token_idx) {
+    t = p->token_idx[r];
+    if (t < 0 || p->T <= t) return 0.0;
+  }
+  const uint16_t* x_row = p->x + p->K * t;
+  const uint16_t* we = p->w + e * p->N * p->K;
+  double acc = 0.0;
+  for (int64_t k = 0; k < p->K; ++k) {
+    uint16_t wv = p->layout == 0 ? we[n * p->K + k] : we[k * p->N + n];
+    acc += operand(x_row[k], p->dtype) * operand(wv, p->dtype);
+  }
+  return acc;
+}
+
+typedef struct {
+  const dense_problem_t* p;
+  int64_t begin, end;
+} dense_slice_t;
+
+static void* run_dense_slice(void* arg) {
+  const dense_slice_t* sl = (const dense_slice_t*)arg;
+  const dense_problem_t* p = sl->p;
+  for (int64_t i = sl->begin; i < sl->end; ++i) {
+    int64_t r = p->pt_r ? p->pt_r[i] : i / p->N;
+    int64_t n = p->pt_r ? p->pt_n[i] : i % p->N;
+    p->y[i] = dense_point(p, r, n);
+  }
+  return NULL;
+}
+
+static int run_dense(const dense_problem_t* p, int nthreads) {
+  if (nthreads <= 0) nthreads = oracle_default_threads();
+  if (nthreads > ORACLE_MAX_THREADS) nthreads = ORACLE_MAX_THREADS;
+  if ((int64_t)nthreads > p->count) nthreads = p->count > 0 ? (int)p->count : 1;
+  pthread_t tid[ORACLE_MAX_THREADS];
+  dense_slice_t sl[ORACLE_MAX_THREADS];
+  int64_t chunk = (p->count + nthreads - 1) / nthreads;
+  int started = 0;
+  for (int t = 0; t < nthreads; ++t) {
+    sl[t].p = p;
+    sl[t].begin = (int64_t)t * chunk;
+    sl[t].end = sl[t].begin + chunk < p->count ? sl[t].begin + chunk : p->count;
+    if (sl[t].begin >= sl[t].end) break;
+    if (t == 0) continue;
+    if (pthread_create(&tid[t], NULL, run_dense_slice, &sl[t]) != 0) {
+      run_dense_slice(&sl[t]);
+      tid[t] = 0;
+    }
+    started = t + 1;
+  }
+  if (p->count > 0) run_dense_slice(&sl[0]);
+  for (int t = 1; t < started; ++t)
+    if (tid[t]) pthread_join(tid[t], NULL);
+  return nthreads;
+}
+
+int oracle_gather_mm(const uint16_t* x, const uint16_t* w, const int32_t* token_idx,
+                     const int32_t* expert_idx, int64_t B, int64_t N, int64_t K, int64_t E,
+                     int64_t T, int dtype, int layout, double* y, int nthreads) {
+  if (B < 0 || N < 0 || K < 1 || E < 1 || T < 0 || (dtype != 0 && dtype != 1) ||
+      (layout != 0 && layout != 1))
+    return -1;
+  dense_problem_t p = {x, w, token_idx, expert_idx, N, K, E, T, dtype, layout, NULL, NULL, B * N, y};
+  return run_dense(&p, nthreads);
+}
+
+int oracle_gather_mm_points(const uint16_t* x, const uint16_t* w, const int32_t* token_idx,
+                            const int32_t* expert_idx, int64_t B, int64_t N, int64_t K, int64_t E,
+                            int64_t T, int dtype, int layout, const int64_t* rows,
+                            const int64_t* cols, int64_t count, double* y, int nthreads) {
+  if (B < 0 || N < 0 || K < 1 || E < 1 || T < 0 || count < 0 || (dtype != 0 && dtype != 1) ||
+      (layout != 0 && layout != 1))
+    return -1;
+  for (int64_t i = 0; i < count; ++i)
+    if (rows[i] < 0 || rows[i] >= B || cols[i] < 0 || cols[i] >= N) return -2;
+  dense_problem_t p = {x, w, token_idx, expert_idx, N, K, E, T, dtype, layout, rows, cols, count, y};
+  return run_dense(&p, nthreads);
 }

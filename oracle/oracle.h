@@ -1,5 +1,6 @@
 /*
- * CPU oracle for the affine group-wise quantized matmul: test infrastructure
+ * CPU oracle for the affine group-wise quantized matmul and the dense grouped
+ * product (gather_mm): test infrastructure
  * only (tests, smoke check, benchmark CPU baseline). See oracle.c for the
  * definition it follows and the readings it takes.
  *
@@ -20,6 +21,10 @@ extern "C" {
 double oracle_bf16_to_f64(uint16_t h);
 uint16_t oracle_f64_to_bf16_rne(double v);
 void oracle_f64_to_bf16_array(const double* v, uint16_t* out, int64_t n);
+double oracle_f16_to_f64(uint16_t h); /* IEEE binary16 bit pattern, exact */
+uint16_t oracle_f64_to_f16_rne(double v);
+void oracle_f64_to_f16_array(const double* v, uint16_t* out, int64_t n);
+void oracle_f16_to_f64_array(const uint16_t* h, double* out, int64_t n);
 uint32_t oracle_code(const uint32_t* row_words, int64_t k, int bits);
 double oracle_weight(const uint32_t* row_words, const uint16_t* row_scales,
                      const uint16_t* row_biases, int64_t k, int bits, int group);
@@ -59,6 +64,19 @@ int oracle_gather_qmm_indexed_points(const uint16_t* x, const uint32_t* w, const
                                      const int32_t* expert_idx, int64_t B, int64_t N, int64_t K,
                                      int64_t E, int64_t T, int bits, int group, const int64_t* rows,
                                      const int64_t* cols, int64_t count, double* y, int nthreads);
+
+/* Dense grouped product: y[B*N], row r reads x row token_idx[r] of x[T, K] (row r
+   when token_idx is NULL) and the weights of expert expert_idx[r]; W is [E, N, K]
+   (layout 0) or [E, K, N] (layout 1); x and W are bf16 (dtype 0) or binary16
+   (dtype 1) bit patterns; zero row if either id is out of range */
+int oracle_gather_mm(const uint16_t* x, const uint16_t* w, const int32_t* token_idx,
+                     const int32_t* expert_idx, int64_t B, int64_t N, int64_t K, int64_t E,
+                     int64_t T, int dtype, int layout, double* y, int nthreads);
+
+int oracle_gather_mm_points(const uint16_t* x, const uint16_t* w, const int32_t* token_idx,
+                            const int32_t* expert_idx, int64_t B, int64_t N, int64_t K, int64_t E,
+                            int64_t T, int dtype, int layout, const int64_t* rows,
+                            const int64_t* cols, int64_t count, double* y, int nthreads);
 
 #ifdef __cplusplus
 }

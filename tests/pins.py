@@ -2,8 +2,9 @@
 
 Each ``check_*`` function takes an oracle object (``oracle.Oracle``) and raises
 AssertionError if it disagrees with what the definition of the computation
-(w = s*q + b per group of 64 along K, y = x . W^T, summed exactly), the bf16
-format, or the documented code layout fix. They run against the real oracle
+(w = s*q + b per group along K, y = x . W^T, summed exactly; for the dense
+grouped product gather_mm, y = x . W^T with W stored [N, K] or [K, N]), the bf16
+and binary16 formats, or the documented code layout fix. They run against the real oracle
 in ``test_oracle_pins.py`` and against oracles with planted mistakes in
 ``test_oracle_mutants.py`` (each planted mistake must trip at least one pin).
 
@@ -67,6 +68,22 @@ def read_bf16_golden():
             if v is None:
                 v = float.fromhex(tok[0])
             rows.append((v, int(tok[1], 16)))
+    return rows
+
+
+def read_f16_golden():
+    """(value, bits, exact) rows of tests/golden/f16_rne.txt."""
+    rows = []
+    with open(os.path.join(GOLDEN, "f16_rne.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            tok = line.split()
+            v = {"inf": np.inf, "-inf": -np.inf, "nan": np.nan, "0": 0.0, "-0": -0.0}.get(tok[0])
+            if v is None:
+                v = float.fromhex(tok[0])
+            rows.append((v, int(tok[1], 16), tok[2] == "exact"))
     return rows
 
 
@@ -390,6 +407,134 @@ def check_indexed_points(O):
     assert np.array_equal(O.gather_qmm_indexed(x, w, s, b, tok, exp, 4, rows=r, cols=c), full[r, c])
 
 
+# ---------------------------------------------------------------------------
+# binary16 and the dense grouped product (gather_mm)
+# ---------------------------------------------------------------------------
+
+def check_f16_golden(O):
+    """Rounding to binary16 and widening back, against hand-derived bit patterns."""
+    for v, bits, exact in read_f16_golden():
+        got = int(O.f64_to_f16(np.array([v]))[0])
+        assert got == bits, f"f16({v!r}) = {got:#06x}, expected {bits:#06x}"
+        if exact:
+            back = float(O.f16_to_f64(np.array([bits], dtype=np.uint16))[0])
+            assert back == v and np.signbit(back) == np.signbit(v), f"f16 {bits:#06x} -> {back!r}"
+
+
+def check_f16_vs_numpy(O):
+    """Widening: every one of the 65536 patterns against numpy's float16. Rounding:
+    numpy converts float64 to float16 to nearest even in one step; random doubles,
+    exact ties and near-ties at every exponent agree bit for bit."""
+    h = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    ref = h.view(np.float16).astype(np.float64)
+    got = O.f16_to_f64(h)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+    rng = np.random.default_rng(21)
+    v = rng.standard_normal(3000) * np.exp2(rng.integers(-30, 18, 3000))
+    fin = ref[np.isfinite(ref)]
+    mids = (np.sort(np.unique(fin))[1:] + np.sort(np.unique(fin))[:-1]) / 2  # exact ties
+    v = np.concatenate([v, mids, np.nextafter(mids, np.inf), np.nextafter(mids, -np.inf)])
+    with np.errstate(over="ignore"):
+        want = v.astype(np.float16).view(np.uint16)
+    assert np.array_equal(O.f64_to_f16(v), want)
+
+
+def _dense_problem(T, B, E, N, K, dtype, layout, seed):
+    """Random x and W (bf16 or binary16 bit patterns), tokens and experts unsorted."""
+    rng = np.random.default_rng(seed)
+    xv = rng.standard_normal((T, K))
+    wshape = (E, N, K) if layout == "nk" else (E, K, N)
+    wv = rng.standard_normal(wshape) * 0.1
+    if dtype == "bf16":
+        x, w = I.to_bf16_bits(xv), I.to_bf16_bits(wv)
+    else:
+        x, w = xv.astype(np.float16).view(np.uint16), wv.astype(np.float16).view(np.uint16)
+    tok = rng.integers(0, T, B).astype(np.int32)
+    exp = rng.integers(0, E, B).astype(np.int32)
+    return x, w, tok, exp
+
+
+def _numpy_operand(h, dtype):
+    return I.bf16_bits_to_f64(h) if dtype == "bf16" else h.view(np.float16).astype(np.float64)
+
+
+def check_gather_mm_brute_force(O):
+    """gather_mm against numpy: rows gathered by fancy indexing, operands widened by
+    numpy (bf16 by a 16-bit shift, binary16 by numpy's own float16), each expert's
+    [N, K] matrix (the [K, N] layout transposed by numpy) in a float64 matmul."""
+    for dtype in ("bf16", "f16"):
+        for layout in ("nk", "kn"):
+            for T, B, E, N, K in ((1, 8, 16, 9, 16), (3, 7, 5, 17, 40), (6, 20, 4, 3, 7)):
+                x, w, tok, exp = _dense_problem(T, B, E, N, K, dtype, layout,
+                                                seed=T * 100 + B + len(dtype) + len(layout))
+                got = O.gather_mm(x, w, tok, exp, dtype, layout)
+                xf = _numpy_operand(x, dtype)
+                wf = _numpy_operand(w, dtype)
+                if layout == "kn":
+                    wf = np.ascontiguousarray(np.transpose(wf, (0, 2, 1)))
+                ref = np.stack([wf[exp[r]] @ xf[tok[r]] for r in range(B)])
+                assert np.allclose(got, ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max()), \
+                    (dtype, layout, T, B)
+                # without a token index, row r reads activation row r
+                assert np.array_equal(O.gather_mm(x[tok], w, None, exp, dtype, layout), got)
+
+
+def check_gather_mm_integer_exact(O):
+    """Integer-valued x and W (exact in both formats): every sum is an integer that
+    int64 arithmetic gives exactly; the two layouts agree with each other."""
+    rng = np.random.default_rng(8)
+    T, B, E, N, K = 5, 12, 3, 11, 48
+    xi = rng.integers(-8, 9, size=(T, K))
+    wi = rng.integers(-8, 9, size=(E, N, K))
+    tok = rng.integers(0, T, B).astype(np.int32)
+    exp = rng.integers(0, E, B).astype(np.int32)
+    want = np.stack([wi[exp[r]] @ xi[tok[r]] for r in range(B)]).astype(np.float64)
+    for dtype in ("bf16", "f16"):
+        if dtype == "bf16":
+            x, w = I.to_bf16_bits(xi.astype(np.float64)), I.to_bf16_bits(wi.astype(np.float64))
+        else:
+            x, w = xi.astype(np.float16).view(np.uint16), wi.astype(np.float16).view(np.uint16)
+        assert np.array_equal(O.gather_mm(x, w, tok, exp, dtype, "nk"), want), dtype
+        wt = np.ascontiguousarray(np.transpose(w, (0, 2, 1)))
+        assert np.array_equal(O.gather_mm(x, wt, tok, exp, dtype, "kn"), want), dtype
+
+
+def check_gather_mm_constant(O):
+    """W[e] = e + 1 everywhere, x[t,:] = (t mod 7) + 1: y[r,n] = K (e_r + 1)((t_r mod 7) + 1)
+    exactly (a mis-gathered token or expert gives a wrong integer); out-of-range ids
+    give zero rows."""
+    T, E, N, K = 9, 6, 5, 32
+    tok = np.array([3, 0, 8, 8, 1, 5, 2, 7, 4, 6, 0, 9, -1, 2], dtype=np.int32)
+    exp = np.array([5, 0, 2, 2, 4, 1, 3, 0, 5, 1, 4, 1, 2, 6], dtype=np.int32)
+    xv = (np.arange(T) % 7 + 1).astype(np.float64)
+    ok = (tok >= 0) & (tok < T) & (exp >= 0) & (exp < E)
+    want = np.where(ok[:, None], K * (exp[:, None] + 1.0) * xv[np.clip(tok, 0, T - 1)][:, None], 0.0)
+    want = want * np.ones((1, N))
+    wv = np.broadcast_to((np.arange(E) + 1.0)[:, None, None], (E, N, K))
+    for dtype in ("bf16", "f16"):
+        enc = I.to_bf16_bits if dtype == "bf16" else (lambda a: np.asarray(a).astype(np.float16).view(np.uint16))
+        x = enc(np.broadcast_to(xv[:, None], (T, K)))
+        w = enc(wv)
+        assert np.array_equal(O.gather_mm(x, w, tok, exp, dtype, "nk"), want), dtype
+        wt = np.ascontiguousarray(np.transpose(w, (0, 2, 1)))
+        assert np.array_equal(O.gather_mm(x, wt, tok, exp, dtype, "kn"), want), dtype
+
+
+def check_gather_mm_points(O):
+    """Point evaluation equals the full result, for either layout and thread count."""
+    for layout in ("nk", "kn"):
+        x, w, tok, exp = _dense_problem(4, 12, 3, 10, 24, "bf16", layout, seed=6)
+        full = O.gather_mm(x, w, tok, exp, "bf16", layout, threads=3)
+        rng = np.random.default_rng(4)
+        r = rng.integers(0, 12, 40)
+        c = rng.integers(0, 10, 40)
+        assert np.array_equal(O.gather_mm(x, w, tok, exp, "bf16", layout, rows=r, cols=c), full[r, c])
+        assert np.array_equal(O.gather_mm(x, w, tok, exp, "bf16", layout, threads=1), full)
+
+
 ALL_CHECKS = [
     check_bf16_golden,
     check_bf16_vs_torch,
@@ -409,4 +554,10 @@ ALL_CHECKS = [
     check_indexed_brute_force,
     check_indexed_constant,
     check_indexed_points,
+    check_f16_golden,
+    check_f16_vs_numpy,
+    check_gather_mm_brute_force,
+    check_gather_mm_integer_exact,
+    check_gather_mm_constant,
+    check_gather_mm_points,
 ]

@@ -43,6 +43,25 @@ MUTANTS = {
     "bf16_ties_away": ("double r = nearbyint(ldexp(a, 8 - e));", "double r = round(ldexp(a, 8 - e));"),
     "token_ignored": ("return dot_row(p->x + t * p->K,", "return dot_row(p->x + r * p->K,"),
     "invalid_token_kept": ("if (t < 0 || t >= p->T) return 0.0;", "if (t < 0 || t >= p->T) t = 0;"),
+    "dense_layout_swapped": ("uint16_t wv = p->layout == 0 ? we[n * p->K + k] : we[k * p->N + n];",
+                             "uint16_t wv = p->layout == 1 ? we[n * p->K + k] : we[k * p->N + n];"),
+    "dense_expert_ignored": ("const uint16_t* we = p->w + e * p->N * p->K;", "const uint16_t* we = p->w;"),
+    "dense_token_ignored": ("const uint16_t* x_row = p->x + p->K * t;",
+                            "const uint16_t* x_row = p->x + p->K * r;"),
+    "dense_invalid_rows_use_expert_0": ("if (e < 0 || p->E <= e) return 0.0;",
+                                        "if (e < 0 || p->E <= e) e = 0;"),
+    "dense_invalid_token_kept": ("if (t < 0 || p->T <= t) return 0.0;", "if (t < 0 || p->T <= t) t = 0;"),
+    "dense_first_k_dropped": ("  for (int64_t k = 0; k < p->K; ++k) {", "  for (int64_t k = 1; k < p->K; ++k) {"),
+    "dense_f16_read_as_bf16": ("return dtype == 0 ? oracle_bf16_to_f64(h) : oracle_f16_to_f64(h);",
+                               "return oracle_bf16_to_f64(h);"),
+    "f16_exponent_bias": ("v = ldexp((double)(1024 + frac), field - 25);",
+                          "v = ldexp((double)(1024 + frac), field - 24);"),
+    "f16_implicit_one_dropped": ("v = ldexp((double)(1024 + frac), field - 25);",
+                                 "v = ldexp((double)(frac), field - 25);"),
+    "f16_subnormal_scale": ("v = ldexp((double)frac, -24);", "v = ldexp((double)frac, -25);"),
+    "f16_truncates": ("double r = nearbyint(ldexp(a, 11 - e));", "double r = floor(ldexp(a, 11 - e));"),
+    "f16_no_overflow": ("if (biased >= 31) return (uint16_t)(sign | 0x7C00u);",
+                        "if (biased >= 32) return (uint16_t)(sign | 0x7C00u);"),
     "bf16_no_overflow": ("if (biased >= 255) return (uint16_t)(sign | 0x7F80u);",
                          "if (biased >= 256) return (uint16_t)(sign | 0x7F80u);"),
 }
