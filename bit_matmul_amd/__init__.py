@@ -36,6 +36,13 @@ BITMM_ERR_LAUNCH = 7
 
 BITMM_OUT_BF16 = 0
 BITMM_OUT_F32 = 1
+BITMM_OUT_F16 = 2
+
+BITMM_DTYPE_BF16 = 0
+BITMM_DTYPE_F16 = 1
+
+BITMM_LAYOUT_NK = 0
+BITMM_LAYOUT_KN = 1
 
 GROUP = 64
 
@@ -43,7 +50,8 @@ __all__ = [
     "BitmmError", "lib", "bitmm_abi_version", "bitmm_status_string", "bitmm_qmv", "bitmm_qmm",
     "bitmm_gather_qmm_workspace_bytes", "bitmm_gather_qmm", "bitmm_gather_qmv",
     "bitmm_gather_qmm_indexed_workspace_bytes", "bitmm_gather_qmm_indexed", "qmv", "qmm",
-    "gather_qmm", "gather_qmv", "gather_qmm_indexed",
+    "gather_qmm", "gather_qmv", "gather_qmm_indexed", "bitmm_gather_mm_workspace_bytes",
+    "bitmm_gather_mm", "gather_mm",
 ]
 
 
@@ -90,6 +98,10 @@ def lib() -> ctypes.CDLL:
         L.bitmm_gather_qmm_indexed.argtypes = [P, P, P, P, P, P, P, I64, I64, I64, I64, I64, I, I,
                                                I, P, SZ, P]
         L.bitmm_gather_qmm_indexed.restype = I
+        L.bitmm_gather_mm_workspace_bytes.argtypes = [I64, I64, I64]
+        L.bitmm_gather_mm_workspace_bytes.restype = SZ
+        L.bitmm_gather_mm.argtypes = [P, P, P, P, P, I64, I64, I64, I64, I64, I, I, I, P, SZ, P]
+        L.bitmm_gather_mm.restype = I
         _lib = L
     return _lib
 
@@ -113,6 +125,10 @@ def bitmm_gather_qmm_indexed_workspace_bytes(B: int, N: int, E: int) -> int:
 # ---------------------------------------------------------------------------
 # Marshalling helpers
 # ---------------------------------------------------------------------------
+
+def bitmm_gather_mm_workspace_bytes(B: int, N: int, E: int) -> int:
+    return int(lib().bitmm_gather_mm_workspace_bytes(int(B), int(N), int(E)))
+
 
 def _torch():
     import torch
@@ -150,6 +166,14 @@ def _out_code(y):
     if y.dtype == torch.float32:
         return BITMM_OUT_F32
     raise TypeError(f"y must be bfloat16 or float32, got {y.dtype}")
+
+
+def _out_code_any(y):
+    """bitmm_out code of y for bitmm_gather_mm (bf16, f32 or float16)."""
+    torch = _torch()
+    if y.dtype == torch.float16:
+        return BITMM_OUT_F16
+    return _out_code(y)
 
 
 def _dense(fn, where, x, w, scales, biases, y, bits, group_size, stream):
@@ -316,4 +340,49 @@ def gather_qmm_indexed(x, w, scales, biases, token_idx, expert_idx, bits: int, o
                                 dtype=torch.uint8, device=x.device)
     bitmm_gather_qmm_indexed(x, w, scales, biases, token_idx, expert_idx, y, workspace, bits,
                              stream=stream)
+    return y, workspace
+
+
+def bitmm_gather_mm(x, w, token_idx, expert_idx, y, workspace, layout: str = "nk", stream=None):
+    """Dense grouped product: y[r, :] = x[token_idx[r], :] * W[expert_idx[r]]^T (rows in any
+    order, token_idx may be None). x and w are both bfloat16 or both float16; w is
+    [E, N, K] (layout "nk") or [E, K, N] ("kn"); y is bfloat16, float16 or float32.
+    Out-of-range ids give zero rows (workspace word 0 flags the first)."""
+    torch = _torch()
+    T, K = x.shape
+    lay = {"nk": BITMM_LAYOUT_NK, "kn": BITMM_LAYOUT_KN}[layout]
+    E = w.shape[0]
+    N = w.shape[1] if lay == BITMM_LAYOUT_NK else w.shape[2]
+    B = expert_idx.shape[0]
+    dev = x.device
+    if x.dtype not in (torch.bfloat16, torch.float16):
+        raise TypeError(f"x must be bfloat16 or float16, got {x.dtype}")
+    dt = BITMM_DTYPE_BF16 if x.dtype == torch.bfloat16 else BITMM_DTYPE_F16
+    _expect(x, "x", x.dtype, (T, K), dev)
+    _expect(w, "w", x.dtype, (E, N, K) if lay == BITMM_LAYOUT_NK else (E, K, N), dev)
+    _expect(expert_idx, "expert_idx", torch.int32, (B,), dev)
+    if token_idx is not None:
+        _expect(token_idx, "token_idx", torch.int32, (B,), dev)
+    _expect(y, "y", y.dtype, (B, N), dev)
+    if workspace.dtype != torch.uint8 or workspace.device != dev or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 tensor on the same device")
+    st = lib().bitmm_gather_mm(_ptr(x), _ptr(w), _ptr(token_idx), _ptr(expert_idx), _ptr(y), B, N,
+                               K, E, T, dt, lay, _out_code_any(y), _ptr(workspace),
+                               workspace.numel(), _stream_ptr(stream, dev))
+    if st != BITMM_OK:
+        raise BitmmError(st, "bitmm_gather_mm")
+    return y
+
+
+def gather_mm(x, w, token_idx, expert_idx, layout: str = "nk", out_dtype=None, workspace=None,
+              stream=None):
+    """Returns (y, workspace); y has x's dtype unless out_dtype is given."""
+    torch = _torch()
+    B, E = expert_idx.shape[0], w.shape[0]
+    N = w.shape[1] if layout == "nk" else w.shape[2]
+    y = torch.empty((B, N), dtype=out_dtype or x.dtype, device=x.device)
+    if workspace is None:
+        workspace = torch.empty(max(bitmm_gather_mm_workspace_bytes(B, N, E), 256),
+                                dtype=torch.uint8, device=x.device)
+    bitmm_gather_mm(x, w, token_idx, expert_idx, y, workspace, layout, stream=stream)
     return y, workspace

@@ -238,4 +238,48 @@ bitmm_status bitmm_gather_qmv(const void* x, const uint32_t* w, const void* scal
   }
 }
 
+size_t bitmm_gather_mm_workspace_bytes(int64_t B, int64_t N, int64_t E) {
+  if (B < 0 || N < 0 || E < 1 || E > INT32_MAX - 2 || B > INT32_MAX) return 0;
+  return bitmm::gather_indexed_workspace_bytes(B, E);
+}
+
+bitmm_status bitmm_gather_mm(const void* x, const void* w, const int32_t* token_idx,
+                             const int32_t* expert_idx, void* y, int64_t B, int64_t N, int64_t K,
+                             int64_t E, int64_t T, bitmm_dtype dtype, bitmm_layout layout,
+                             bitmm_out out, void* workspace, size_t workspace_bytes, void* stream) {
+  try {
+    if (dtype != BITMM_DTYPE_BF16 && dtype != BITMM_DTYPE_F16) return BITMM_ERR_UNSUPPORTED;
+    if (layout != BITMM_LAYOUT_NK && layout != BITMM_LAYOUT_KN) return BITMM_ERR_UNSUPPORTED;
+    if (out != BITMM_OUT_BF16 && out != BITMM_OUT_F32 && out != BITMM_OUT_F16)
+      return BITMM_ERR_UNSUPPORTED;
+    if (B < 0 || N < 0 || T < 0 || K < 1 || E < 1) return BITMM_ERR_SHAPE;
+    if (B > INT32_MAX || N > INT32_MAX || K > INT32_MAX || T > INT32_MAX || E > INT32_MAX - 2)
+      return BITMM_ERR_SHAPE;
+    // The tile's k-steps are 16 wide; [K, N] rows are copied in 16-byte chunks; the
+    // per-expert counters live in LDS; offsets into x and into one expert's W are 32-bit.
+    if (K % 16 != 0 || (layout == BITMM_LAYOUT_KN && N % 8 != 0) ||
+        E > bitmm::gather_indexed_max_experts() || T * K * 2 > (int64_t)INT32_MAX ||
+        N * K * 2 > (int64_t)INT32_MAX)
+      return BITMM_ERR_UNSUPPORTED;
+    if (B == 0 || N == 0) return BITMM_OK;
+    if ((T > 0 && !x) || !w || !expert_idx || !y) return BITMM_ERR_NULL;
+    if (!workspace || workspace_bytes < bitmm_gather_mm_workspace_bytes(B, N, E))
+      return BITMM_ERR_WORKSPACE;
+    if (!aligned(x, 16) || !aligned(w, 16) || !aligned(expert_idx, 4) || !aligned(token_idx, 4) ||
+        !aligned(workspace, 16) || !aligned(y, out == BITMM_OUT_F32 ? 4 : 2))
+      return BITMM_ERR_ALIGN;
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    bitmm_status st = device_check(hs);
+    if (st != BITMM_OK) return st;
+    const int otype = out == BITMM_OUT_F32 ? bitmm::kOutF32 : (out == BITMM_OUT_F16 ? bitmm::kOutF16 : bitmm::kOutBf16);
+    hipError_t e = bitmm::launch_gather_mm(static_cast<const uint16_t*>(x),
+                                           static_cast<const uint16_t*>(w), token_idx, expert_idx,
+                                           y, B, N, K, E, T, (int)dtype, (int)layout, otype,
+                                           workspace, hs);
+    return e == hipSuccess ? BITMM_OK : BITMM_ERR_LAUNCH;
+  } catch (...) {
+    return BITMM_ERR_LAUNCH;
+  }
+}
+
 }  // extern "C"

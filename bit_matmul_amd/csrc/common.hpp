@@ -142,6 +142,14 @@ __device__ __forceinline__ void dma(__amdgpu_buffer_rsrc_t r, uint32_t voff, cha
 // "memory" clobber keeps the compiler from moving memory accesses across it.
 __device__ __forceinline__ void barrier_no_fence() { asm volatile("s_barrier" ::: "memory"); }
 
+// Workgroups are dealt round-robin to the 8 XCDs, each with its own L2. Remaps the
+// hardware id so that every XCD gets a contiguous run of logical ids: neighbouring
+// logical tiles (which share operands) then run on one XCD and meet in its L2.
+__device__ __forceinline__ int xcd_remap(int b, int total) {
+  if (total % 8 != 0) return b;
+  return (b % 8) * (total / 8) + b / 8;
+}
+
 // Cache-policy operand of a buffer load: non-temporal (data read once).
 constexpr int kNonTemporal = 2;
 

@@ -102,7 +102,7 @@ __device__ void block_exclusive_scan(int* v, int n, int* part) {
 __global__ __launch_bounds__(kPrepThreads) void gather_sort_kernel(const int32_t* __restrict__ tok,
                                                                    const int32_t* __restrict__ exp,
                                                                    int B, int E, int T, int N,
-                                                                   int out_f32, void* __restrict__ y,
+                                                                   int ysz, void* __restrict__ y,
                                                                    uint32_t* __restrict__ ws) {
   __shared__ int cnt[kMaxIndexedExperts + 1];
   __shared__ int part[kPrepThreads];
@@ -132,8 +132,8 @@ __global__ __launch_bounds__(kPrepThreads) void gather_sort_kernel(const int32_t
     perm[atomicAdd(&cnt[ok ? e : E], 1)] = r;
     if (!ok) {
       for (int n = 0; n < N; ++n) {
-        if (out_f32)
-          static_cast<float*>(y)[(int64_t)r * N + n] = 0.f;
+        if (ysz == 4)
+          static_cast<uint32_t*>(y)[(int64_t)r * N + n] = 0u;
         else
           static_cast<uint16_t*>(y)[(int64_t)r * N + n] = 0;
       }
@@ -155,11 +155,6 @@ struct GatherParams {
   int tiles_n;
   int out_f32;
 };
-
-__device__ __forceinline__ int xcd_remap(int b, int total) {
-  if (total % 8 != 0) return b;
-  return (b % 8) * (total / 8) + b / 8;
-}
 
 template <int BITS, typename T>
 __global__ __launch_bounds__(T::THREADS) void gather_qmm_kernel(GatherParams p) {
@@ -327,15 +322,23 @@ size_t gather_indexed_workspace_bytes(int64_t B, int64_t E) {
 
 int64_t gather_indexed_max_experts() { return kMaxIndexedExperts; }
 
+hipError_t launch_gather_sort(const int32_t* token_idx, const int32_t* expert_idx, int64_t B,
+                              int64_t E, int64_t T, int64_t N, int ysz, void* y, void* workspace,
+                              hipStream_t stream) {
+  hipLaunchKernelGGL(gather_sort_kernel, dim3(1), dim3(kPrepThreads), 0, stream, token_idx,
+                     expert_idx, (int)B, (int)E, (int)T, (int)N, ysz, y,
+                     static_cast<uint32_t*>(workspace));
+  return hipGetLastError();
+}
+
 hipError_t launch_gather_qmm_indexed(const uint16_t* x, const uint32_t* w, const uint16_t* scales,
                                      const uint16_t* biases, const int32_t* token_idx,
                                      const int32_t* expert_idx, void* y, int64_t B, int64_t N,
                                      int64_t K, int64_t E, int64_t T, int bits, int group,
                                      bool out_f32, void* workspace, hipStream_t stream) {
   uint32_t* ws = static_cast<uint32_t*>(workspace);
-  hipLaunchKernelGGL(gather_sort_kernel, dim3(1), dim3(kPrepThreads), 0, stream, token_idx,
-                     expert_idx, (int)B, (int)E, (int)T, (int)N, out_f32 ? 1 : 0, y, ws);
-  hipError_t err = hipGetLastError();
+  hipError_t err = launch_gather_sort(token_idx, expert_idx, B, E, T, N, out_f32 ? 4 : 2, y, workspace,
+                                      stream);
   if (err != hipSuccess) return err;
   GatherParams p;
   p.x = x;

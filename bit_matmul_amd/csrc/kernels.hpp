@@ -8,6 +8,9 @@
 
 namespace bitmm {
 
+// Output element types of the matrix-core epilogue (bitmm_out's values).
+enum OutType { kOutBf16 = 0, kOutF32 = 1, kOutF16 = 2 };
+
 // GEMV / small-M path: y[M, N] = x[M, K] * dequant(w)^T, rows taken 8 at a time.
 hipError_t launch_qmv(const uint16_t* x, const uint32_t* w, const uint16_t* scales,
                       const uint16_t* biases, void* y, int64_t M, int64_t N, int64_t K, int bits,
@@ -44,5 +47,20 @@ hipError_t launch_gather_qmm_indexed(const uint16_t* x, const uint32_t* w, const
                                      const int32_t* expert_idx, void* y, int64_t B, int64_t N,
                                      int64_t K, int64_t E, int64_t T, int bits, int group,
                                      bool out_f32, void* workspace, hipStream_t stream);
+
+// Counting sort of B output rows by expert into the indexed-gather workspace layout
+// (word 0 status, offsets [E+1], permutation [B]); rows with an out-of-range token or
+// expert id are written as zeros in y (ysz bytes per element).
+hipError_t launch_gather_sort(const int32_t* token_idx, const int32_t* expert_idx, int64_t B,
+                              int64_t E, int64_t T, int64_t N, int ysz, void* y, void* workspace,
+                              hipStream_t stream);
+
+// Dense grouped product (gather_mm): the counting sort above, then the grouped
+// matrix-core kernel over bf16 (dtype 0) or binary16 (dtype 1) operands, W stored
+// [E, N, K] (layout 0) or [E, K, N] (layout 1); otype 0 bf16, 1 f32, 2 binary16.
+hipError_t launch_gather_mm(const uint16_t* x, const uint16_t* w, const int32_t* token_idx,
+                            const int32_t* expert_idx, void* y, int64_t B, int64_t N, int64_t K,
+                            int64_t E, int64_t T, int dtype, int layout, int otype,
+                            void* workspace, hipStream_t stream);
 
 }  // namespace bitmm

@@ -35,10 +35,9 @@
 #include <type_traits>
 
 #include "common.hpp"
+#include "tile_epilogue.hpp"
 
 namespace bitmm {
-
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 // f(integral_constant<int, I>) for I = B .. E-1, in order, each a separate instantiation.
 template <int B, int E, typename F>
@@ -409,51 +408,9 @@ struct MmTile4 {
     // reads the activation buffers any more once all have passed this barrier.
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     barrier_no_fence();
-    // Epilogue: lane (c, h) holds rows 8 (j/4) + 4 h + j%4 of column c in each 32x32 block.
-    // (Offsets recomputed from an opaque lane index, as at the top.)
-    int etid = threadIdx.x;
-    asm volatile("" : "+v"(etid));
-    const int elane = etid & 63, elc = elane & 31, elh = elane >> 5;
-    const int col = col0 + elc;
-    const bool packed = !out_f32 && (N % 8) == 0 && (reinterpret_cast<uintptr_t>(y_rows) & 15) == 0 &&
-                        col0 + 32 <= N;  // wave-uniform
-    if (packed) {
-      // bf16 through this wave's LDS region (BM rows x 64 bytes), then 16-byte stores
-      // of 8 columns each: 20 stores per 320 rows instead of 160 two-byte ones. Row r
-      // sits at row slot r ^ ((r >> 2) & 1), so the two 32-lane halves of a write
-      // (rows r and r+4) and the four rows of a 16-lane read hit distinct banks.
-      char* tile = lds + wave * (BM * 64);
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const int r = mb * 32 + 8 * (j >> 2) + 4 * elh + (j & 3);
-          *reinterpret_cast<uint16_t*>(tile + (r ^ ((r >> 2) & 1)) * 64 + elc * 2) = f32_to_bf16(acc[mb][j]);
-        }
-      }
-#pragma unroll
-      for (int t = 0; t < BM / 16; ++t) {
-        const int r = 16 * t + (elane >> 2);
-        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(tile + (r ^ ((r >> 2) & 1)) * 64 + (elane & 3) * 16);
-        if (r < rows)
-          *reinterpret_cast<u32x4_t*>(static_cast<char*>(y_rows) + ((int64_t)(RMAP ? perm[r] : r) * N + col0 + (elane & 3) * 8) * 2) = v;
-      }
-    } else if (col < N) {
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const int r = mb * 32 + 8 * (j >> 2) + 4 * elh + (j & 3);
-          if (r < rows) {
-            const int64_t o = (int64_t)(RMAP ? perm[r] : r) * N + col;
-            if (out_f32)
-              static_cast<float*>(y_rows)[o] = acc[mb][j];
-            else
-              static_cast<uint16_t*>(y_rows)[o] = f32_to_bf16(acc[mb][j]);
-          }
-        }
-      }
-    }
+    // Epilogue through this wave's region of the (now idle) activation buffers.
+    store_tile<MB, RMAP>(acc, rows, col0, N, y_rows, out_f32 ? kOutF32 : kOutBf16, lds + wave * (BM * 64),
+                         perm);
   }
 };
 

@@ -19,19 +19,12 @@ struct QmmParams {
   int out_f32;
 };
 
-// Workgroups are dealt round-robin to the 8 XCDs, each with its own L2. Remap the
-// hardware id so every XCD gets a contiguous run of logical tiles, ordered M-fastest:
-// the M tiles that share one weight column block then run on the same XCD and read
-// its codes from that XCD's L2 instead of HBM.
-__device__ __forceinline__ int xcd_remap(int b, int total) {
-  if (total % 8 != 0) return b;
-  return (b % 8) * (total / 8) + b / 8;
-}
-
 template <typename T>
 __global__ __launch_bounds__(T::THREADS) void qmm_mfma_kernel(QmmParams p) {
   __shared__ __attribute__((aligned(16))) char lds[T::LDS_BYTES];
   const int total = p.tiles_m * p.tiles_n;
+  // Logical tiles are ordered M-fastest, so the M tiles that share one weight column
+  // block run on one XCD and read its codes from that XCD's L2 instead of HBM.
   const int L = xcd_remap(blockIdx.x, total);
   const int tm = L % p.tiles_m;
   const int tn = L / p.tiles_m;

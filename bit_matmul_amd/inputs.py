@@ -22,7 +22,7 @@ top-8 routing, expert dims 2816 / 704, 573 prompt tokens). Every draw uses
 stream per tensor:
 
     tag 1 = activations, 2 = codes, 3 = scales, 4 = routing, 5 = second
-    activations (MoE down-projection input)
+    activations (MoE down-projection input), 6 = dense weights (gather_mm)
 
 Value distributions: scale ~ U[0.001, 0.02] rounded to bf16; bias =
 -2**(bits-1) * scale (exact in bf16); codes uniform over [0, 2**bits); dense
@@ -40,6 +40,7 @@ TAG_Q = 2
 TAG_SCALE = 3
 TAG_ROUTE = 4
 TAG_X2 = 5
+TAG_W = 6
 
 
 def rng_for(seed: int, tag: int, *extra: int) -> np.random.Generator:
@@ -78,6 +79,19 @@ def to_bf16_bits(a) -> np.ndarray:
     bits = np.where(nz, bits, 0)
     bits = bits | np.where(np.signbit(a), 0x8000, 0)
     return bits.astype(np.uint16)
+
+
+def f32_to_bf16_bits(a) -> np.ndarray:
+    """Round float32 values to bf16 (nearest, ties to even) -> uint16 bits, for large
+    draws made in float32 (bf16 is the upper half of a binary32). Finite inputs only."""
+    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
+    r = (u >> np.uint32(16)) & np.uint32(1)
+    return ((u + np.uint32(0x7FFF) + r) >> np.uint32(16)).astype(np.uint16)
+
+
+def to_f16_bits(a) -> np.ndarray:
+    """Round values to IEEE binary16 with numpy (nearest, ties to even) -> uint16 bits."""
+    return np.asarray(a).astype(np.float16).view(np.uint16)
 
 
 def bf16_bits_to_f64(bits) -> np.ndarray:
@@ -193,6 +207,97 @@ class GatherIndexed:
 
     def flops(self) -> int:
         return 2 * self.B * self.N * self.K
+
+
+class GatherMM:
+    """Dense grouped product: y[r,:] = x[token_idx[r],:] . W[expert_idx[r]]^T, rows in any
+    order (token_idx None: row r reads x row r). x and w are bf16 (dtype "bf16") or
+    binary16 ("f16") bit patterns; w is [E, N, K] (layout "nk") or [E, K, N] ("kn")."""
+
+    def __init__(self, name, x, w, token_idx, expert_idx, dtype: str = "bf16", layout: str = "nk"):
+        self.name = name
+        self.x, self.w = x, w
+        self.token_idx, self.expert_idx = token_idx, expert_idx
+        self.dtype, self.layout = dtype, layout
+        self.T, self.K = x.shape
+        self.E = w.shape[0]
+        self.N = w.shape[1] if layout == "nk" else w.shape[2]
+        self.B = expert_idx.shape[0]
+        assert x.dtype == np.uint16 and w.dtype == np.uint16 and dtype in ("bf16", "f16")
+        assert w.shape == ((self.E, self.N, self.K) if layout == "nk" else (self.E, self.K, self.N))
+        assert expert_idx.dtype == np.int32
+        assert token_idx is None or (token_idx.shape == (self.B,) and token_idx.dtype == np.int32)
+
+    def algorithmic_bytes(self, out_bytes: int = 2) -> int:
+        """Weights of every distinct expert the rows use (streamed once), the activation
+        rows they read, the ids and the outputs."""
+        used = np.unique(self.expert_idx[(self.expert_idx >= 0) & (self.expert_idx < self.E)])
+        rows = self.T if self.token_idx is None else np.unique(self.token_idx).size
+        ids = self.expert_idx.nbytes + (0 if self.token_idx is None else self.token_idx.nbytes)
+        return used.size * self.w[0].nbytes + rows * self.K * 2 + ids + self.B * self.N * out_bytes
+
+    def flops(self) -> int:
+        return 2 * self.B * self.N * self.K
+
+
+def _encode(a, dtype: str) -> np.ndarray:
+    return to_bf16_bits(a) if dtype == "bf16" else to_f16_bits(a)
+
+
+def random_gather_mm(T: int, B: int, E: int, N: int, K: int, dtype: str = "bf16",
+                     layout: str = "nk", seed: int = 0, with_tokens: bool = True) -> GatherMM:
+    """Arbitrary dense grouped product: random token and expert per row (repeats, any
+    order); x ~ N(0, 1), W ~ N(0, 0.02^2) like a trained projection."""
+    rng = rng_for(seed, TAG_ROUTE, 11, T, B, E, N, K)
+    exp = rng.integers(0, E, B).astype(np.int32)
+    tok = rng.integers(0, T, B).astype(np.int32) if with_tokens else None
+    rows = T if with_tokens else B
+    x = _encode(rng_for(seed, TAG_X, 11, rows, K).standard_normal(size=(rows, K)), dtype)
+    wshape = (E, N, K) if layout == "nk" else (E, K, N)
+    w = _encode(0.02 * rng_for(seed, TAG_W, E, N, K).standard_normal(size=wshape), dtype)
+    return GatherMM(f"gather_mm_T{rows}_B{B}_E{E}_K{K}_N{N}_{dtype}_{layout}", x, w, tok, exp,
+                    dtype, layout)
+
+
+def moe_gather_mm(which: str, dtype: str = "bf16", layout: str = "nk", seed: int = 0,
+                  tokens: int = None, E: int = None, top_k: int = None, hidden: int = None,
+                  inter: int = None) -> GatherMM:
+    """The MoE prefill of a non-quantized checkpoint: the routing of ``moe_gather`` (573
+    tokens, 8 of 128 experts each) in routing (token-major) order, dense weights.
+
+    ``which="up"``:   K=hidden, N=inter; x = the hidden states [tokens, hidden], read
+                      through the token index.
+    ``which="down"``: K=inter, N=hidden; x = one N(0,1) row per output row [B, inter].
+    Weights ~ N(0, 0.02^2), drawn in float32 and rounded to the operand type.
+    """
+    tokens = MOE_TOKENS if tokens is None else tokens
+    E = MOE_E if E is None else E
+    top_k = MOE_TOPK if top_k is None else top_k
+    hidden = MOE_HIDDEN if hidden is None else hidden
+    inter = MOE_INTER if inter is None else inter
+    idx, tok = moe_routing(seed, tokens, E, top_k)
+    order = np.argsort(tok.astype(np.int64) * (E + 1) + idx, kind="stable")
+    exp = np.ascontiguousarray(idx[order])
+    B = exp.shape[0]
+    enc32 = f32_to_bf16_bits if dtype == "bf16" else to_f16_bits
+    if which == "up":
+        K, N = hidden, inter
+        x = enc32(rng_for(seed, TAG_X, 6, tokens, hidden).standard_normal(size=(tokens, hidden),
+                                                                          dtype=np.float32))
+        tk = np.ascontiguousarray(tok[order])
+    elif which == "down":
+        K, N = inter, hidden
+        x = enc32(rng_for(seed, TAG_X2, 6, B, inter).standard_normal(size=(B, inter), dtype=np.float32))
+        tk = None
+    else:
+        raise ValueError("which must be 'up' or 'down'")
+    wshape = (E, N, K) if layout == "nk" else (E, K, N)
+    w32 = rng_for(seed, TAG_W, E, N, K).standard_normal(size=wshape, dtype=np.float32)
+    w32 *= np.float32(0.02)
+    w = enc32(w32)
+    del w32
+    return GatherMM(f"gather_mm_{which}_B{B}_E{E}_K{K}_N{N}_{dtype}_{layout}", x, w, tk, exp,
+                    dtype, layout)
 
 
 def _dense_weights(seed: int, N: int, K: int, bits: int, sub: int = 0, group: int = GROUP):

@@ -15,7 +15,9 @@
  *     y[r][n] = sum_k x[r][k] * w[e_r][n][k],
  *     w[e][n][k] = s[e][n][k/gs] * q[e][n][k] + b[e][n][k/gs],   gs = group_size,
  *
- * with e_r = 0 for the dense forms and e_r = expert_idx[r] for the gathered one.
+ * with e_r = 0 for the dense forms and e_r = expert_idx[r] for the gathered one. The
+ * same PR's non-quantized MoE path, gather_mm, is bitmm_gather_mm at the end of this
+ * file: the grouped product over plain bf16 or binary16 weights.
  *
  * Storage (all row-major, contiguous, little-endian):
  *   x        bf16 [M, K]                 (activations; bf16 passed as uint16 bits)
@@ -64,7 +66,8 @@ typedef enum {
   BITMM_ERR_SHAPE = 2,       /* M, N, B < 0; K < 1; E < 1; K not a multiple of 64 and of
                                 group_size                                                  */
   BITMM_ERR_UNSUPPORTED = 3, /* bits not in {4, 8}; group_size not in {32, 64, 128}; unknown
-                                output type                                                 */
+                                output type, operand type or layout; a size limit stated
+                                at the entry point                                          */
   BITMM_ERR_ALIGN = 4,       /* x, w or workspace not 16-byte aligned; scales or biases not
                                 2-byte aligned; y not aligned to its element size;
                                 expert_idx not 4-byte aligned                               */
@@ -73,7 +76,16 @@ typedef enum {
   BITMM_ERR_LAUNCH = 7       /* a kernel launch reported an error                           */
 } bitmm_status;
 
-typedef enum { BITMM_OUT_BF16 = 0, BITMM_OUT_F32 = 1 } bitmm_out;
+/* Output element type. BITMM_OUT_F16 (IEEE binary16, rounded to nearest even) is
+   accepted by bitmm_gather_mm only. */
+typedef enum { BITMM_OUT_BF16 = 0, BITMM_OUT_F32 = 1, BITMM_OUT_F16 = 2 } bitmm_out;
+
+/* Operand element type of bitmm_gather_mm (x and w alike). */
+typedef enum { BITMM_DTYPE_BF16 = 0, BITMM_DTYPE_F16 = 1 } bitmm_dtype;
+
+/* Storage of each expert's weight matrix for bitmm_gather_mm: [N, K] (one row per output
+   column, K contiguous; the MoE layer's own layout) or [K, N] (N contiguous). */
+typedef enum { BITMM_LAYOUT_NK = 0, BITMM_LAYOUT_KN = 1 } bitmm_layout;
 
 /* Version of this interface (BITMM_ABI_VERSION). */
 int bitmm_abi_version(void);
@@ -182,6 +194,38 @@ bitmm_status bitmm_gather_qmv(const void* x, const uint32_t* w, const void* scal
                               const int32_t* expert_idx, void* y, int64_t B, int64_t N, int64_t K,
                               int64_t E, int64_t T, int bits, int group_size, bitmm_out out,
                               void* stream);
+
+/*
+ * Bytes of device workspace bitmm_gather_mm needs for B rows, N columns and E experts
+ * (a multiple of 256; 0 if an argument is negative or E < 1).
+ */
+size_t bitmm_gather_mm_workspace_bytes(int64_t B, int64_t N, int64_t E);
+
+/*
+ * Dense grouped product for non-quantized MoE layers (gather_mm). PR #1562 ("The branch
+ * is live") notes that every non-quantized MoE checkpoint reaches the grouped GEMM
+ * through SwitchLinear::Regular::forward, with no gate, and its tests check gather_mm
+ * against an f64 dense per-expert product in both operand layouts and in f32, bf16 and
+ * f16. The same scheduler as bitmm_gather_qmm_indexed, without dequantization:
+ *   y[r, :] = x[t_r, :] * W[expert_idx[r]]^T for r in [0, B),
+ *   t_r = token_idx[r], or r when token_idx is NULL.
+ *   x: [T, K] and w: [E, N, K] (layout BITMM_LAYOUT_NK) or [E, K, N] (BITMM_LAYOUT_KN),
+ *   both of type `dtype` (bf16 or binary16 bit patterns); token_idx (optional),
+ *   expert_idx: int32 [B], any order, repeats allowed; y: [B, N] of type `out` (bf16,
+ *   f32 or binary16, independent of `dtype`).
+ * Products of the operands are exact in f32 and accumulation is f32 (matrix cores).
+ * Rows with an out-of-range token or expert id are written as zeros and workspace word 0
+ * (uint32) receives 1 + the first such row (0 if none). `workspace`: caller-owned device
+ * memory of at least bitmm_gather_mm_workspace_bytes(B, N, E) bytes, 16-byte aligned, no
+ * initialisation needed; two calls sharing it must be ordered on one stream.
+ * Limits (else BITMM_ERR_UNSUPPORTED): K a multiple of 16; with BITMM_LAYOUT_KN, N a
+ * multiple of 8; E <= 8192; T * K * 2 < 2^31 and N * K * 2 < 2^31 (one expert's weights).
+ * f32 operands are not supported (BITMM_ERR_UNSUPPORTED for any other dtype).
+ */
+bitmm_status bitmm_gather_mm(const void* x, const void* w, const int32_t* token_idx,
+                             const int32_t* expert_idx, void* y, int64_t B, int64_t N, int64_t K,
+                             int64_t E, int64_t T, bitmm_dtype dtype, bitmm_layout layout,
+                             bitmm_out out, void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -31,6 +31,16 @@ def bf16_tensor(a_u16):
     return t.from_numpy(np.ascontiguousarray(a_u16).view(np.int16)).view(t.bfloat16).to(dev())
 
 
+def f16_tensor(a_u16):
+    t = torch()
+    return t.from_numpy(np.ascontiguousarray(a_u16).view(np.int16)).view(t.float16).to(dev())
+
+
+def half_tensor(a_u16, dtype):
+    """bf16 ("bf16") or binary16 ("f16") bit patterns as a device tensor of that type."""
+    return bf16_tensor(a_u16) if dtype == "bf16" else f16_tensor(a_u16)
+
+
 def u32_tensor(a_u32):
     t = torch()
     return t.from_numpy(np.ascontiguousarray(a_u32).view(np.int32)).to(dev())

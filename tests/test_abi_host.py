@@ -46,7 +46,8 @@ def test_exports_every_declared_function(L):
     assert set(names) == {"bitmm_abi_version", "bitmm_status_string", "bitmm_qmv", "bitmm_qmm",
                           "bitmm_gather_qmm_workspace_bytes", "bitmm_gather_qmm",
                           "bitmm_gather_qmv", "bitmm_gather_qmm_indexed_workspace_bytes",
-                          "bitmm_gather_qmm_indexed"}
+                          "bitmm_gather_qmm_indexed", "bitmm_gather_mm_workspace_bytes",
+                          "bitmm_gather_mm"}
     for n in names:
         assert hasattr(L, n), f"libbitmm.so does not export {n}"
 
@@ -60,7 +61,8 @@ def test_abi_version_matches_header(L):
 def test_status_codes_match_header_and_have_strings(L):
     codes = header_enum("BITMM")
     for k, v in codes.items():
-        if k.startswith("BITMM_OUT_"):
+        if k.startswith(("BITMM_OUT_", "BITMM_DTYPE_", "BITMM_LAYOUT_")):
+            assert getattr(bm, k) == v, k
             continue
         assert getattr(bm, k) == v, k
         s = bm.bitmm_status_string(v)
@@ -265,6 +267,74 @@ def test_gather_qmm_indexed_validation(L, kw, expected):
             pytest.skip("fake pointers would reach a real device")
         expected = bm.BITMM_ERR_DEVICE
     assert L.bitmm_gather_qmm_indexed(*gidx_args(**kw)) == expected
+
+
+def gmm_args(**kw):
+    a = dict(x=A, w=A + 0x1000, tok=A + 0x4000, idx=A + 0x5000, y=A + 0x6000, B=4584, N=704,
+             K=2816, E=128, T=573, dtype=0, layout=0, out=0, ws=A + 0x7000, ws_bytes=1 << 20,
+             stream=0)
+    a.update(kw)
+    return [ctypes.c_void_p(a["x"]), ctypes.c_void_p(a["w"]), ctypes.c_void_p(a["tok"]),
+            ctypes.c_void_p(a["idx"]), ctypes.c_void_p(a["y"]), a["B"], a["N"], a["K"], a["E"],
+            a["T"], a["dtype"], a["layout"], a["out"], ctypes.c_void_p(a["ws"]), a["ws_bytes"],
+            ctypes.c_void_p(a["stream"])]
+
+
+GMM_CASES = [
+    (dict(dtype=2), bm.BITMM_ERR_UNSUPPORTED),
+    (dict(dtype=-1), bm.BITMM_ERR_UNSUPPORTED),
+    (dict(layout=2), bm.BITMM_ERR_UNSUPPORTED),
+    (dict(out=3), bm.BITMM_ERR_UNSUPPORTED),
+    (dict(K=100), bm.BITMM_ERR_UNSUPPORTED),              # K a multiple of 16
+    (dict(layout=1, N=700), bm.BITMM_ERR_UNSUPPORTED),    # [K, N] rows of 16-byte chunks
+    (dict(layout=0, N=700), None),                         # [N, K]: any N
+    (dict(E=8193), bm.BITMM_ERR_UNSUPPORTED),
+    (dict(T=1 << 20, K=1024), bm.BITMM_ERR_UNSUPPORTED),  # activation offsets are 32-bit
+    (dict(N=1 << 17, K=1 << 14), bm.BITMM_ERR_UNSUPPORTED),  # one expert's W over 2 GiB
+    (dict(E=0), bm.BITMM_ERR_SHAPE),
+    (dict(K=0), bm.BITMM_ERR_SHAPE),
+    (dict(T=-1), bm.BITMM_ERR_SHAPE),
+    (dict(B=-1), bm.BITMM_ERR_SHAPE),
+    (dict(N=-1), bm.BITMM_ERR_SHAPE),
+    (dict(B=0), bm.BITMM_OK),
+    (dict(N=0, layout=1), bm.BITMM_OK),
+    (dict(idx=0), bm.BITMM_ERR_NULL),
+    (dict(w=0), bm.BITMM_ERR_NULL),
+    (dict(y=0), bm.BITMM_ERR_NULL),
+    (dict(x=0), bm.BITMM_ERR_NULL),
+    (dict(x=0, T=0, tok=0, B=4), None),                  # no activation rows: x unused
+    (dict(ws=0), bm.BITMM_ERR_WORKSPACE),
+    (dict(ws_bytes=4 * (4584 + 130) - 1), bm.BITMM_ERR_WORKSPACE),
+    (dict(ws=A + 4), bm.BITMM_ERR_ALIGN),
+    (dict(tok=A + 1), bm.BITMM_ERR_ALIGN),
+    (dict(w=A + 8), bm.BITMM_ERR_ALIGN),
+    (dict(x=A + 8), bm.BITMM_ERR_ALIGN),
+    (dict(y=A + 2, out=1), bm.BITMM_ERR_ALIGN),
+    (dict(y=A + 2, out=2), None),
+    (dict(dtype=1, layout=1, out=2), None),
+    (dict(), None),
+    (dict(tok=0, T=4584), None),
+]
+
+
+@pytest.mark.parametrize("kw,expected", GMM_CASES)
+def test_gather_mm_validation(L, kw, expected):
+    if expected is None:
+        if gpu_present():
+            pytest.skip("fake pointers would reach a real device")
+        expected = bm.BITMM_ERR_DEVICE
+    assert L.bitmm_gather_mm(*gmm_args(**kw)) == expected
+
+
+def test_gather_mm_workspace_size(L):
+    ws = bm.bitmm_gather_mm_workspace_bytes
+    assert ws(4584, 704, 128) >= 4 * (4584 + 128 + 2)
+    assert ws(4584, 704, 128) % 256 == 0
+    assert ws(-1, 1, 1) == 0 and ws(1, 1, 0) == 0
+    need = ws(4584, 704, 128)
+    if not gpu_present():
+        assert L.bitmm_gather_mm(*gmm_args(ws_bytes=need)) == bm.BITMM_ERR_DEVICE
+    assert L.bitmm_gather_mm(*gmm_args(ws_bytes=need - 1)) == bm.BITMM_ERR_WORKSPACE
 
 
 def test_indexed_workspace_size(L):
