@@ -20,8 +20,10 @@ Also reported: ``cpu_baseline``, the CPU oracle timed on the host cores on a
 bounded sample of the same workload, and ``suite``, every other workload of the
 hot path (the 8-bit GEMV, the prefill GEMM at M = 600 and M = 3, 4- and 8-bit,
 the MoE expert-gathered GEMM in both orientations, sorted and in routing order through
-the indexed entry point, and the MoE decode step's gathered GEMV at 1 and 4 tokens in
-both orientations), timed the same way.
+the indexed entry point, also at a 46-token prompt below the grouped path's gate, the
+MoE decode step's gathered GEMV at 1 and 4 tokens in both orientations, and the dense
+grouped product of a non-quantized MoE layer, bf16, both orientations and both weight
+layouts), timed the same way.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-suite] [--no-cpu]
                        [--calibrate-copy]
@@ -94,12 +96,18 @@ class Case:
         def i32(a):
             return torch.from_numpy(np.ascontiguousarray(a).view(np.int32)).to(dev)
 
-        base = [bf16(problem.x), i32(problem.w), bf16(problem.scales), bf16(problem.biases)]
         self.ids = None
+        if kind == "gather_mm":
+            def half(a):
+                t = torch.from_numpy(np.ascontiguousarray(a).view(np.int16))
+                return t.view(torch.bfloat16 if problem.dtype == "bf16" else torch.float16).to(dev)
+            base = [half(problem.x), half(problem.w)]
+        else:
+            base = [bf16(problem.x), i32(problem.w), bf16(problem.scales), bf16(problem.biases)]
         if kind == "gather":
             base.append(i32(problem.expert_idx))
             rows = problem.B
-        elif kind in ("gather_qmv", "gather_indexed"):
+        elif kind in ("gather_qmv", "gather_indexed", "gather_mm"):
             # the ids stay put: each step's rows read a different copy of every tensor
             self.ids = (None if problem.token_idx is None else i32(problem.token_idx),
                         i32(problem.expert_idx))
@@ -122,6 +130,9 @@ class Case:
             elif kind == "gather_indexed":
                 ws = torch.empty(bm.bitmm_gather_qmm_indexed_workspace_bytes(problem.B, problem.N, problem.E),
                                  dtype=torch.uint8, device=dev)
+            elif kind == "gather_mm":
+                ws = torch.empty(bm.bitmm_gather_mm_workspace_bytes(problem.B, problem.N, problem.E),
+                                 dtype=torch.uint8, device=dev)
             self.sets.append((ts, y, ws))
         self.bm = bm
         self.i = 0
@@ -138,6 +149,8 @@ class Case:
             bm.bitmm_gather_qmv(*ts, *self.ids, y, p.bits)
         elif self.kind == "gather_indexed":
             bm.bitmm_gather_qmm_indexed(*ts, *self.ids, y, ws, p.bits)
+        elif self.kind == "gather_mm":
+            bm.bitmm_gather_mm(*ts, *self.ids, y, ws, p.layout)
         else:
             bm.bitmm_gather_qmm(*ts, y, ws, p.bits)
 
@@ -300,7 +313,11 @@ def main():
                  ("gather_indexed", lambda: I.moe_prefill_indexed("up")),
                  ("gather_indexed", lambda: I.moe_prefill_indexed("down")),
                  ("gather_qmv", lambda: I.moe_decode("up", 1)), ("gather_qmv", lambda: I.moe_decode("down", 1)),
-                 ("gather_qmv", lambda: I.moe_decode("up", 4)), ("gather_qmv", lambda: I.moe_decode("down", 4))]
+                 ("gather_qmv", lambda: I.moe_decode("up", 4)), ("gather_qmv", lambda: I.moe_decode("down", 4)),
+                 ("gather_indexed", lambda: I.moe_prefill_indexed("up", tokens=46)),
+                 ("gather_indexed", lambda: I.moe_prefill_indexed("down", tokens=46)),
+                 ("gather_mm", lambda: I.moe_gather_mm("up")), ("gather_mm", lambda: I.moe_gather_mm("down")),
+                 ("gather_mm", lambda: I.moe_gather_mm("up", layout="kn"))]
         for kind, make in specs:
             p = make()
             c = Case(torch, p, kind, torch.bfloat16)

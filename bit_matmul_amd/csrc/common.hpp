@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace bitmm {
 
 constexpr int kWave = 64;    // CDNA wavefront width
@@ -141,6 +143,15 @@ __device__ __forceinline__ void dma(__amdgpu_buffer_rsrc_t r, uint32_t voff, cha
 // (s_waitcnt vmcnt) and consume every LDS read they issue before arriving here. The
 // "memory" clobber keeps the compiler from moving memory accesses across it.
 __device__ __forceinline__ void barrier_no_fence() { asm volatile("s_barrier" ::: "memory"); }
+
+// f(integral_constant<int, I>) for I = B .. E-1, in order, each a separate instantiation.
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
 
 // Workgroups are dealt round-robin to the 8 XCDs, each with its own L2. Remaps the
 // hardware id so that every XCD gets a contiguous run of logical ids: neighbouring

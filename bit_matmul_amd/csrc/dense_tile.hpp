@@ -7,21 +7,21 @@
 // shapes each expert's W feeds only its few dozen rows, about 36 flop per byte of W,
 // far below the matrix cores' ridge. So the tile is built around the copy shape:
 //   * Both operands go HBM -> LDS by direct buffer loads (no registers), K in stages of
-//     128: per stage a 128-row x 256-byte W tile and a BM-row x 256-byte activation
-//     tile, three stages in LDS, copies two stages ahead. Every copy instruction moves
-//     1 KB as 4 rows x 256 contiguous bytes.
+//     KS = 64 or 128: per stage a W tile of 128 columns and a BM-row activation tile,
+//     NS stages in LDS, copies NS-1 stages ahead. Every copy instruction moves 1 KB
+//     (4 rows x 256 bytes, or 8 x 128 for row-contiguous tiles at KS = 64).
 //   * W stored [N, K] (layout 0) and the activations are row-contiguous tiles: 16-byte
-//     chunk c of tile row r sits at position c ^ (r & 15), so the 16 rows one MFMA
+//     chunk c of tile row r sits at position c ^ swz(r), so the 16 rows one MFMA
 //     operand quarter reads hit distinct banks. The MFMA operands are 16-byte LDS
 //     reads: lane (c, h) of k-step u reads chunk 2u + h of its row.
-//   * W stored [K, N] (layout 1) arrives as 128 k-rows x 128 columns; chunk c of k-row r
+//   * W stored [K, N] (layout 1) arrives as KS k-rows x 128 columns; chunk c of k-row r
 //     sits at position c ^ 4(r & 3). The B operand comes from transposing LDS reads
 //     (ds_read_b64_tr_b16): within each 16-lane group, lane m points at k-row m/4,
 //     columns 4(m%4) .. +3, and lane i receives column i at the four k-rows, which is
 //     the MFMA's layout (lane (c, h): column c, k = 16u + 8h .. +7).
 // Four waves, one per SIMD, each owning 32 columns and all BM = 32 MB rows; f32
 // accumulation in 32x32x16 MFMAs (bf16 or f16 inputs, exact products).
-// K a multiple of 16: the last stage runs (K mod 128)/16 k-steps; the bytes its copies
+// K a multiple of 16: the last stage runs (K mod KS)/16 k-steps; the bytes its copies
 // bring from past K (the next row, or zeros past the tensor) are never multiplied.
 #pragma once
 
@@ -34,26 +34,28 @@ typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
-template <int DT, int LAYOUT, int MB>
+template <int DT, int LAYOUT, int MB, int KS = 128, int NS = 3>
 struct MmTileD {
   static constexpr int WAVES = 4;
   static constexpr int THREADS = 64 * WAVES;
   static constexpr int BM = 32 * MB;
   static constexpr int BN = 32 * WAVES;
-  static constexpr int KS = 128;                // k per stage
-  static constexpr int NS = 3;                  // stages in LDS (copies NS-1 ahead)
-  static constexpr int WB = BN * KS * 2;        // W tile: 128 rows of 256 bytes
-  static constexpr int XB = BM * KS * 2;        // activation tile: BM rows of 256 bytes
+  static constexpr int ROWB = KS * 2;           // bytes of a row-contiguous tile row
+  static constexpr int CPR = ROWB / 16;         // 16-byte chunks per such row
+  static constexpr int WB = BN * KS * 2;        // W tile (either layout)
+  static constexpr int XB = BM * ROWB;          // activation tile
   static constexpr int SB = WB + XB;
   static constexpr int LDS_BYTES = NS * SB;
   static constexpr int CW = WB / 1024 / WAVES;  // 1 KB copies per wave and stage
   static constexpr int CX = XB / 1024 / WAVES;
   static constexpr int C = CW + CX;
   static_assert(DT == 0 || DT == 1, "operand type");
+  static_assert(KS == 64 || KS == 128, "stage depth");
+  static_assert(NS >= 2, "stages");
   static_assert(LAYOUT == 0 || LAYOUT == 1, "weight layout");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
   static_assert(WAVES * BM * 64 <= LDS_BYTES, "epilogue scratch");
-  static_assert(C <= 31, "vmcnt range");
+  static_assert((NS - 2) * C <= 63, "vmcnt range");
 
   __device__ static __forceinline__ f32x16_t mfma(u32x4_t a, u32x4_t b, f32x16_t c) {
     if constexpr (DT == 0)
@@ -63,6 +65,11 @@ struct MmTileD {
       return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a),
                                                     __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
   }
+
+  // Position of chunk c of row r of a row-contiguous tile: c ^ swz(r). 256-byte rows
+  // start on the same bank, so 16 consecutive rows take 16 distinct positions; 128-byte
+  // rows alternate between two bank halves, so pairs of rows share a position.
+  __device__ static __forceinline__ int swz(int r) { return ROWB == 256 ? (r & 15) : ((r >> 1) & 7); }
 
   // x: [T, K]; tile row r (< rows) is output row perm[r] and reads activation row
   // tok[perm[r]] (perm[r] when tok is null). we: the expert's W, [N, K] or [K, N].
@@ -90,27 +97,30 @@ struct MmTileD {
         LAYOUT == 0 ? make_rsrc(we + (int64_t)n0 * K, (int64_t)(N - n0) * K * 2)
                     : make_rsrc(we + n0, ((int64_t)K * N - n0) * 2);
     // Per-lane byte offsets of the copies of stage 0; stage s adds s * (w_step, x_step).
-    // Copy j of a stage covers tile rows 4j .. 4j+3; lane L carries row 4j + L/16 into
-    // position L % 16, i.e. the chunk the swizzle puts there.
-    const int L16 = lane & 15;
+    // A copy moves 1 KB: rows of a row-contiguous tile (ROWB bytes each), or 4 k-rows of
+    // 256 bytes of a [K, N] tile; lane L carries chunk (L mod chunks per row) of its row
+    // into that position, i.e. the chunk the swizzle puts there.
     uint32_t wo[CW], xo[CX];
 #pragma unroll
     for (int jj = 0; jj < CW; ++jj) {
-      const int r = 4 * (wave + jj * WAVES) + (lane >> 4);
-      if constexpr (LAYOUT == 0)
-        wo[jj] = (uint32_t)(r * K * 2 + ((L16 ^ (r & 15)) << 4));
-      else
-        wo[jj] = (uint32_t)(r * N * 2 + ((L16 ^ (4 * (r & 3))) << 4));
+      const int j = wave + jj * WAVES;
+      if constexpr (LAYOUT == 0) {
+        const int r = (1024 / ROWB) * j + lane / CPR, p = lane % CPR;
+        wo[jj] = (uint32_t)(r * K * 2 + ((p ^ swz(r)) << 4));
+      } else {
+        const int r = 4 * j + (lane >> 4), p = lane & 15;
+        wo[jj] = (uint32_t)(r * N * 2 + ((p ^ (4 * (r & 3))) << 4));
+      }
     }
 #pragma unroll
     for (int kk = 0; kk < CX; ++kk) {
-      const int r = 4 * (wave + kk * WAVES) + (lane >> 4);
+      const int r = (1024 / ROWB) * (wave + kk * WAVES) + lane / CPR, p = lane % CPR;
       int src = 0;
       if (r < rows) {
         src = perm[r];
         if (tok) src = tok[src];
       }
-      xo[kk] = r < rows ? (uint32_t)(src * K * 2 + ((L16 ^ (r & 15)) << 4)) : 0x80000000u;
+      xo[kk] = r < rows ? (uint32_t)(src * K * 2 + ((p ^ swz(r)) << 4)) : 0x80000000u;
     }
     const uint32_t w_step = LAYOUT == 0 ? KS * 2 : (uint32_t)KS * N * 2;
     constexpr uint32_t x_step = KS * 2;
@@ -125,10 +135,10 @@ struct MmTileD {
 
     // Operand read offsets within a stage. Row-contiguous tiles: lane (c, h) at k-step u
     // reads chunk 2u + h of row c (plus 32 mb rows, or the wave's 32 W rows) at position
-    // (2u + h) ^ (c & 15) = 2u ^ q, q = h ^ (c & 15).
-    const int q = lh ^ (lc & 15);
-    const int arow = lc * 256;
-    const int brow = (32 * wave + lc) * 256;
+    // (2u + h) ^ swz(c) = 2u ^ q, q = h ^ swz(c) (swz(c) equals swz of those rows).
+    const int q = lh ^ swz(lc);
+    const int arow = lc * ROWB;
+    const int brow = (32 * wave + lc) * ROWB;
     // Transposing reads (layout 1): lane m of 16-lane group g of half h points at
     // k-row 16u + 8h + 4 t2 + m/4, columns 32 wave + 16 g + 4 (m%4) .. +3.
     const int tm = lane & 15, tg = (lane >> 4) & 1;
@@ -157,24 +167,27 @@ struct MmTileD {
       }
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
-        const u32x4_t av = *reinterpret_cast<const u32x4_t*>(xsb + mb * 8192 + arow + po);
+        const u32x4_t av = *reinterpret_cast<const u32x4_t*>(xsb + mb * 32 * ROWB + arow + po);
         acc[mb] = mfma(av, bv, acc[mb]);
       }
     };
 
     const int S = (K + KS - 1) / KS;
-    copy_stage(0, 0);
-    if (S > 1) copy_stage(1, 1);
+#pragma unroll
+    for (int i = 0; i < NS - 1; ++i)
+      if (i < S) copy_stage(i, i);
 #pragma unroll 1
     for (int s = 0; s < S; ++s) {
-      // This wave's copies of stage s have landed (those of stage s+1 may still fly);
-      // after the barrier every wave's have, and every wave is done with stage s-1.
-      if (s + 1 < S)
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(C) : "memory");
-      else
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      // This wave's copies of stage s have landed (those of the min(NS-2, S-1-s) stages
+      // after it may still fly); after the barrier every wave's have, and every wave is
+      // done with stage s-1, whose buffer the copies issued next overwrite.
+      const int ahead = min(NS - 2, S - 1 - s);
+      static_for<0, NS - 1>([&](auto Jc) {
+        constexpr int J = decltype(Jc)::value;
+        if (ahead == J) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(J * C) : "memory");
+      });
       barrier_no_fence();
-      if (s + 2 < S) copy_stage(s + 2, (s + 2) % NS);
+      if (s + NS - 1 < S) copy_stage(s + NS - 1, (s + NS - 1) % NS);
       const int b = __builtin_amdgcn_readfirstlane((s % NS) * SB);
       const char* wsb = lds + b;
       const char* xsb = lds + b + WB;

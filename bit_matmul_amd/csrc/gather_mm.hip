@@ -53,13 +53,26 @@ hipError_t launch_tiles(GmmParams p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Stage depth. 64-k stages (72 KB of LDS at two row blocks) let two workgroups share a
+// CU, so one's start-up and epilogue overlap the other's stream; 128-k stages keep the
+// 256-byte row copies of [N, K] storage (64-k stages copy 8 rows x 128 bytes, which
+// streams slower) but allow one workgroup per CU. Measured on the MoE shapes
+// (bf16, 128 experts, ~36 rows each): [N, K] K = 2816: 109 us at 128-k stages, 115 at
+// 64; K = 704 (six stages per tile): 133 against 113; [K, N] (256-byte k-rows either
+// way): 106 / 100 and 132 / 115.
+template <int DT, int LAYOUT, int MB>
+hipError_t launch_ks(GmmParams p, hipStream_t stream) {
+  if (LAYOUT == 0 && p.K >= 2048) return launch_tiles<MmTileD<DT, LAYOUT, MB, 128, 3>>(p, stream);
+  return launch_tiles<MmTileD<DT, LAYOUT, MB, 64, 3>>(p, stream);
+}
+
 // Row blocks per tile from the mean rows per expert, with slack for the routing spread:
 // one 32-row block up to ~25 rows, else two (experts with more loop over row tiles).
 template <int DT, int LAYOUT>
 hipError_t launch_mb(GmmParams p, hipStream_t stream) {
   const int64_t mean = (p.B + p.E - 1) / p.E;
-  if (mean + mean / 4 <= 32) return launch_tiles<MmTileD<DT, LAYOUT, 1>>(p, stream);
-  return launch_tiles<MmTileD<DT, LAYOUT, 2>>(p, stream);
+  if (mean + mean / 4 <= 32) return launch_ks<DT, LAYOUT, 1>(p, stream);
+  return launch_ks<DT, LAYOUT, 2>(p, stream);
 }
 
 }  // namespace

@@ -32,21 +32,10 @@
 // + (b - 64 s); rounded to bf16 for the MFMA; f32 accumulation.
 #pragma once
 
-#include <type_traits>
-
 #include "common.hpp"
 #include "tile_epilogue.hpp"
 
 namespace bitmm {
-
-// f(integral_constant<int, I>) for I = B .. E-1, in order, each a separate instantiation.
-template <int B, int E, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-  if constexpr (B < E) {
-    f(std::integral_constant<int, B>{});
-    static_for<B + 1, E>(f);
-  }
-}
 
 // SBM chooses where a wave finds the scales and biases of its 32 weight rows:
 //   0: two 2-byte loads per group and lane, into registers, PD groups ahead;

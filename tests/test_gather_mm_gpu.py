@@ -62,10 +62,12 @@ def ref(g, token_idx="same", expert_idx=None, rows=None, cols=None):
 
 # (T, B, E, N, K): a few rows per expert (one 32-row block), ~36 per expert (two
 # blocks), ~100 per expert (the row-tile loop); K with a full last stage (K % 128 == 0)
-# and with 1, 4 and 7 of its 8 k-steps; N ragged against the 128-column block, the
+# and with a ragged last stage (64-k stages below K = 2048 for [N, K] storage and
+# always for [K, N]; 128-k stages above); N ragged against the 128-column block, the
 # 32-column wave slice and 8 (the 16-byte output stores).
 SHAPES = [(10, 40, 16, 96, 128), (50, 576, 16, 130, 704), (64, 300, 3, 70, 1808),
-          (40, 360, 10, 200, 2816), (30, 200, 5, 64, 144), (7, 9, 4, 8, 16), (20, 64, 2, 136, 1040)]
+          (40, 360, 10, 200, 2816), (30, 200, 5, 64, 144), (7, 9, 4, 8, 16), (20, 64, 2, 136, 1040),
+          (12, 50, 4, 72, 2064)]
 
 
 @pytest.mark.parametrize("layout", ["nk", "kn"])
