@@ -194,6 +194,10 @@ __device__ __forceinline__ bool gemv_row(const GemvBatch& bt, int K, int N, bool
   return true;
 }
 
+// log2 of a quantization group size (32, 64 or 128): the GEMV kernels index scales with
+// shifts, since an integer division ahead of their first loads delays every wave.
+inline int group_shift(int group) { return group == 32 ? 5 : (group == 64 ? 6 : 7); }
+
 // Grid rows of a launch: one per gathered output row, or one.
 inline unsigned gemv_grid_rows(const GemvBatch& bt) { return bt.exp ? (unsigned)bt.rows : 1u; }
 

@@ -68,7 +68,7 @@ hipError_t launch_rows(const uint16_t* x, const uint32_t* w, const uint16_t* sca
     dp.y = y;
     dp.N = (int)N;
     dp.K = (int)K;
-    dp.group = group;
+    dp.gshift = group_shift(group);
     dp.out_f32 = out_f32 ? 1 : 0;
     dp.steps_per_wave = dp.total_steps = 0;
     dp.bt = bt;
@@ -86,7 +86,7 @@ hipError_t launch_rows(const uint16_t* x, const uint32_t* w, const uint16_t* sca
     sp.y = y;
     sp.N = (int)N;
     sp.K = (int)K;
-    sp.group = group;
+    sp.gshift = group_shift(group);
     sp.out_f32 = out_f32 ? 1 : 0;
     sp.bt = bt;
     return bits == 4 ? qmv_split_detail::launch_bits<4>(sp, (int)M, stream)
@@ -107,7 +107,7 @@ hipError_t launch_rows(const uint16_t* x, const uint32_t* w, const uint16_t* sca
     p.y = static_cast<char*>(y) + (size_t)(m0 * N) * ysz;
     p.N = (int)N;
     p.K = (int)K;
-    p.group = group;
+    p.gshift = group_shift(group);
     p.out_f32 = out_f32 ? 1 : 0;
     p.bt = bt;
     const hipError_t e = bits == 4 ? qmv_detail::launch_bits<4>(p, mr, cpl, stream)

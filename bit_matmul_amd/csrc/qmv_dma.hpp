@@ -35,7 +35,7 @@ struct Params {
   const uint16_t* b;
   void* y;
   int N, K;
-  int group;           // quantization group along K: 32, 64 or 128
+  int gshift;    // log2 of the quantization group along K (5, 6 or 7: groups of 32, 64, 128)
   int out_f32;
   int steps_per_wave;  // consecutive steps each wave owns
   int total_steps;     // ceil(N / R)
@@ -77,7 +77,7 @@ __global__ __launch_bounds__(kThreads) void qmv_dma_kernel(Params p) {
   const int slast = active ? min(step0 + SPW, p.total_steps) - 1 : p.total_steps - 1;
   const int N = p.N, K = p.K;
   const int nch = K / T::CC;          // chunks per row
-  const int G = K / p.group;           // scales (and biases) per weight row
+  const int G = K >> p.gshift;           // scales (and biases) per weight row
   const int64_t rowbytes = (int64_t)K * BITS / 8;
   const int r = lane / L;             // row of the step
   const int li = lane % L;
@@ -102,7 +102,7 @@ __global__ __launch_bounds__(kThreads) void qmv_dma_kernel(Params p) {
     const int c = li + L * m;
     const bool ok = c < nch;
     coff[m] = ok ? (uint32_t)(r * rowbytes + c * 16) : kNoChunk;
-    soff[m] = ok ? (uint32_t)((r * G + c * T::CC / p.group) * 2) : kNoChunk;
+    soff[m] = ok ? (uint32_t)((r * G + ((c * T::CC) >> p.gshift)) * 2) : kNoChunk;
   }
   struct Step {
     u32x4_t q[C];

@@ -30,7 +30,7 @@ struct QmvParams {
   const uint16_t* b;
   void* y;
   int N, K;
-  int group;     // quantization group along K: 32, 64 or 128
+  int gshift;    // log2 of the quantization group along K (5, 6 or 7: groups of 32, 64, 128)
   int out_f32;
   GemvBatch bt;  // gathered rows (blockIdx.y, one activation row each), or none
 };
@@ -57,7 +57,7 @@ __global__ __launch_bounds__(kQmvThreads) void qmv_kernel(QmvParams p) {
   }
   if (n0 >= p.N) return;  // uniform per wave
   const int nch = p.K / CC;
-  const int G = p.K / p.group;  // scales (and biases) per weight row
+  const int G = p.K >> p.gshift;  // scales (and biases) per weight row
   const int64_t wrow = (int64_t)p.K * BITS / 32;
 
   // Rows past N repeat the last row (loads stay in bounds); they are not stored.
@@ -92,7 +92,7 @@ __global__ __launch_bounds__(kQmvThreads) void qmv_kernel(QmvParams p) {
       const int c = kb + i * kWave + lane;
       ok[i] = c < nch;
       const int cc = ok[i] ? c : nch - 1;
-      const int g = cc * CC / p.group;
+      const int g = (cc * CC) >> p.gshift;
 #pragma unroll
       for (int r = 0; r < RPW; ++r) {
         q[i][r] = load_stream(wr[r] + 4 * (int64_t)cc);

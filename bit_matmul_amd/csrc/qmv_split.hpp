@@ -37,7 +37,7 @@ struct Params {
   const uint16_t* b;
   void* y;
   int N, K;
-  int group;     // quantization group along K: 32, 64 or 128
+  int gshift;    // log2 of the quantization group along K (5, 6 or 7: groups of 32, 64, 128)
   int out_f32;
   GemvBatch bt;  // gathered rows (blockIdx.y), or none
 };
@@ -70,7 +70,7 @@ __global__ __launch_bounds__(64 * MAXW) void qmv_split_kernel(Params p) {
   const int li = lane & 31;
   const int K = p.K, N = p.N;
   const int nch = K / CC;
-  const int G = K / p.group;  // scales (and biases) per weight row
+  const int G = K >> p.gshift;  // scales (and biases) per weight row
   const int c = wave * 32 + li;
   const bool ok = c < nch;
   const int64_t rowbytes = (int64_t)K * BITS / 8;
@@ -90,7 +90,7 @@ __global__ __launch_bounds__(64 * MAXW) void qmv_split_kernel(Params p) {
   sq = uniform_ptr(sq);
   bq = uniform_ptr(bq);
   const uint32_t voff = ok ? (uint32_t)(r * rowbytes + c * 16) : kNoChunk;
-  const uint32_t soff = ok ? (uint32_t)((r * G + c * CC / p.group) * 2) : kNoChunk;
+  const uint32_t soff = ok ? (uint32_t)((r * G + ((c * CC) >> p.gshift)) * 2) : kNoChunk;
 
   // Codes, scales and biases of one block of RW rows. Rows past N, and chunks past the
   // row end, read as zeros through the descriptors (a block past the last one reads
