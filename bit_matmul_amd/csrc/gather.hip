@@ -245,7 +245,9 @@ hipError_t launch_grouped(GatherParams p, hipStream_t stream) {
 }
 
 // Scales and biases staged in LDS once per workgroup when the wave's block fits (G <= 48),
-// with 4-byte copies when G is even and both arrays 4-byte aligned.
+// with 4-byte copies when G is even and both arrays 4-byte aligned. Weights in
+// 16-row x 64-byte loads (WS), four groups ahead: 1-5 % faster than 32 x 32-byte loads
+// three groups ahead on the MoE shapes.
 template <int BITS, typename T, bool RMAP>
 hipError_t launch_form(GatherParams p, hipStream_t stream) {
   if constexpr (RMAP)
@@ -260,12 +262,12 @@ hipError_t launch_sb(GatherParams p, hipStream_t stream) {
   const bool wide = G % 2 == 0 && (reinterpret_cast<uintptr_t>(p.s) & 3) == 0 &&
                     (reinterpret_cast<uintptr_t>(p.b) & 3) == 0;
   if (G <= 12)
-    return wide ? launch_form<BITS, MmTile4<BITS, MB, 4, 3, 2, 1, 12, RMAP>, RMAP>(p, stream)
-                : launch_form<BITS, MmTile4<BITS, MB, 4, 3, 2, 2, 12, RMAP>, RMAP>(p, stream);
+    return wide ? launch_form<BITS, MmTile4<BITS, MB, 4, 4, 2, 1, 12, RMAP, true>, RMAP>(p, stream)
+                : launch_form<BITS, MmTile4<BITS, MB, 4, 4, 2, 2, 12, RMAP, true>, RMAP>(p, stream);
   if (G <= 48)
-    return wide ? launch_form<BITS, MmTile4<BITS, MB, 4, 3, 2, 1, 48, RMAP>, RMAP>(p, stream)
-                : launch_form<BITS, MmTile4<BITS, MB, 4, 3, 2, 2, 48, RMAP>, RMAP>(p, stream);
-  return launch_form<BITS, MmTile4<BITS, MB, 4, 3, 2, 0, 0, RMAP>, RMAP>(p, stream);
+    return wide ? launch_form<BITS, MmTile4<BITS, MB, 4, 4, 2, 1, 48, RMAP, true>, RMAP>(p, stream)
+                : launch_form<BITS, MmTile4<BITS, MB, 4, 4, 2, 2, 48, RMAP, true>, RMAP>(p, stream);
+  return launch_form<BITS, MmTile4<BITS, MB, 4, 4, 2, 0, 0, RMAP, true>, RMAP>(p, stream);
 }
 
 // One row of 4 waves, each with 32 weight rows: every expert's weights are dequantized

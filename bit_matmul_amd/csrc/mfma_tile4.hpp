@@ -14,7 +14,9 @@
 //   * Weights go straight from HBM to registers: lane (c, h) of wave wn holds, for group
 //     g, the 16 bytes (4-bit) or 32 bytes (8-bit) of weight row n0 + 32 wn + c that hold
 //     codes 32h .. 32h+31 of the group, plus the group's scale and bias. Loads for group
-//     g+3 are issued while group g is multiplied. No LDS traffic, no barrier.
+//     g+PD are issued while group g is multiplied. No LDS traffic, no barrier. With WS
+//     the loads read 16 rows x 64 contiguous bytes per instruction and one lane swap
+//     per register puts the bytes in that layout.
 //   * Activations are the only operand staged in LDS (three buffers of one group, BM rows
 //     x 128 bytes, copied HBM -> LDS without passing through registers, two groups ahead).
 //     One barrier per group.
@@ -48,7 +50,12 @@ namespace bitmm {
 // RMAP: tile rows are gathered. Tile row i is output row perm[i] of y[., N], and it
 // reads activation row tok[perm[i]] of x[T, K] (row perm[i] when tok is null); without
 // RMAP, tile row i is row i of both x_rows and y_rows.
-template <int BITS, int MB, int WN, int PD = 3, int XD = 2, int SBM = 0, int GMAX = 0, bool RMAP = false>
+// WS: weight loads of 16 rows x 64 contiguous bytes (rows 0-15 and 16-31 of the wave's
+// block in two instructions) instead of 32 rows x 32 bytes, redistributed to the
+// MFMA layout with v_permlane16_swap (see load_w); 4-bit needs an even PD (each pair
+// of instructions carries two groups) and XD = 2.
+template <int BITS, int MB, int WN, int PD = 3, int XD = 2, int SBM = 0, int GMAX = 0, bool RMAP = false,
+          bool WS = false>
 struct MmTile4 {
   static constexpr int WAVES = WN;
   static constexpr int THREADS = 64 * WAVES;
@@ -73,6 +80,7 @@ struct MmTile4 {
   static_assert(XI % WAVES == 0, "every wave issues the same number of copies");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
   static_assert(PD >= 2 && XD >= 1 && XD <= PD, "prefetch depths");
+  static_assert(!WS || BITS == 8 || (PD % 2 == 0 && XD == 2), "paired weight loads");
   // Loads issued after the copies of group g+1, when body g waits for them: the weight
   // loads of that body and the copies and weight loads of the XD-1 bodies after it.
   static constexpr int VM_AFTER_COPY = WL + (XD - 1) * (XC + WL);
@@ -161,6 +169,14 @@ struct MmTile4 {
       }
     }
     const uint32_t woff = (uint32_t)(lc * rowbytes + lh * 16 * WV);
+    // WS: lane (m, q) = (lane % 16, lane / 16) loads chunk c(q) of a 64-byte span of row m
+    // (first instruction) and of row 16 + m (second); c(q) = q at 8 bits (the span is one
+    // group) and 0, 2, 1, 3 at 4 bits (two groups: the swap must leave chunk h of each
+    // group in lane half h).
+    const int wq = lane >> 4;
+    const int wchunk = BITS == 8 ? wq : (((wq & 1) << 1) | (wq >> 1));
+    const uint32_t wsx = (uint32_t)((lane & 15) * rowbytes + wchunk * 16);
+    const uint32_t wsy = wsx + (uint32_t)(16 * rowbytes);
     const uint32_t soff = (uint32_t)((lc * GS + glane) * 2);
     // Activation read offsets within a buffer for k-step u (row lc of row block 0).
     int aoff[4];
@@ -171,13 +187,46 @@ struct MmTile4 {
     // again shortly after, from L2.
     auto load_w = [&](int g, Wraw& r) {
       const int gc = min(g, G - 1);  // past the end: a valid group, never used
+      if constexpr (WS && BITS == 8) {
+        r.q[0] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rw, wsx, gc * GB, 0));
+        r.q[1] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rw, wsy, gc * GB, 0));
+      } else {
 #pragma unroll
-      for (int v = 0; v < WV; ++v)
-        r.q[v] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
-                                                 rw, woff + v * 16, gc * GB, 0));
+        for (int v = 0; v < WV; ++v)
+          r.q[v] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                                   rw, woff + v * 16, gc * GB, 0));
+      }
       if constexpr (SBM == 0) {
         r.s = __builtin_amdgcn_raw_buffer_load_b16(rs, soff, gidx_uniform(gc) * 2, 0);
         r.b = __builtin_amdgcn_raw_buffer_load_b16(rb, soff, gidx_uniform(gc) * 2, 0);
+      }
+    };
+    // WS, 4 bits: groups ge, ge+1 (ge even) of rows 0-15 and 16-31. The 64-byte span may
+    // pass the row end when ge = G-1; its offset is in the checked per-lane part, so
+    // past the last row of W it reads zeros.
+    auto load_pair = [&](int ge, Wraw& r0, Wraw& r1) {
+      const uint32_t go = (uint32_t)(min(ge, (G - 1) & ~1) * GB);
+      r0.q[0] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rw, wsx + go, 0, 0));
+      r1.q[0] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rw, wsy + go, 0, 0));
+      if constexpr (SBM == 0) {
+        r0.s = __builtin_amdgcn_raw_buffer_load_b16(rs, soff, gidx_uniform(min(ge, G - 1)) * 2, 0);
+        r0.b = __builtin_amdgcn_raw_buffer_load_b16(rb, soff, gidx_uniform(min(ge, G - 1)) * 2, 0);
+        r1.s = __builtin_amdgcn_raw_buffer_load_b16(rs, soff, gidx_uniform(min(ge + 1, G - 1)) * 2, 0);
+        r1.b = __builtin_amdgcn_raw_buffer_load_b16(rb, soff, gidx_uniform(min(ge + 1, G - 1)) * 2, 0);
+      }
+    };
+    // Redistribution after the WS loads. v_permlane16_swap exchanges lanes 16-31 of its
+    // first operand with lanes 0-15 of its second, and 48-63 with 32-47 (lane layout
+    // checked on the device). For instructions X (rows 0-15) and Y (rows 16-31) as
+    // loaded, lane (c, h) afterwards holds, of row c, chunk h of group ge in X and chunk
+    // h of group ge+1 in Y (4 bits), or chunks 2h and 2h+1 of the group (8 bits): exactly
+    // the non-WS layout.
+    auto wswap = [&](u32x4_t& a, u32x4_t& b) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const auto r = __builtin_amdgcn_permlane16_swap(a[e], b[e], false, false);
+        a[e] = r[0];
+        b[e] = r[1];
       }
     };
     // Staged scales and biases: this wave's region, value of row lc and group g.
@@ -266,8 +315,13 @@ struct MmTile4 {
     for (int i = 0; i < XD; ++i)
 #pragma unroll
       for (int k = 0; k < XC; ++k) copy_x(i, xb + i * XB, k);
+    if constexpr (WS && BITS == 4) {
 #pragma unroll
-    for (int i = 0; i < PD; ++i) load_w(i, wr[i]);
+      for (int i = 0; i < PD; i += 2) load_pair(i, wr[i], wr[i + 1]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < PD; ++i) load_w(i, wr[i]);
+    }
     if constexpr (SBM != 0) {
       // Lane L of copy j carries values 64 j + L (2-byte form) or 128 j + 2 L, +1 (4-byte
       // form) of the wave's block; rows past N read as zeros.
@@ -291,6 +345,8 @@ struct MmTile4 {
       wr[0].s = s0;
       wr[0].b = b0;
     }
+    if constexpr (WS && BITS == 4) wswap(wr[0].q[0], wr[1].q[0]);
+    if constexpr (WS && BITS == 8) wswap(wr[0].q[0], wr[0].q[1]);
     Aff acur = affine(wr[0]);
     u32x4_t bcur;
     {
@@ -308,7 +364,7 @@ struct MmTile4 {
     auto body = [&](auto Ic, int g) {
       constexpr int I = decltype(Ic)::value;
       const Wraw& wc = wr[I];
-      const Wraw& wn = wr[(I + 1) % PD];
+      Wraw& wn = wr[(I + 1) % PD];
       uint32_t sn = 0, bn = 0;  // staged scale and bias of group g+1
       if constexpr (SBM != 0) sb_read(g + 1, sn, bn);
       // Buffer of group g and of group g + XD: scalar byte offsets.
@@ -343,8 +399,15 @@ struct MmTile4 {
 #pragma unroll
         for (int k = 0; k < XC; ++k)
           if (k * (3 * MB) / XC == p) copy_x(g + XD, xdst, k);
-        // Weight loads of group g+PD once the codes of group g are spent (step 3).
-        if (p == 3 * MB) load_w(g + PD, wr[I]);
+        // Weight loads of group g+PD once the codes of group g are spent (step 3); paired
+        // 4-bit loads go out from odd bodies, for groups g+PD-1 and g+PD.
+        if (p == 3 * MB) {
+          if constexpr (WS && BITS == 4) {
+            if constexpr (I % 2 == 1) load_pair(g + PD - 1, wr[(I + PD - 1) % PD], wr[I]);
+          } else {
+            load_w(g + PD, wr[I]);
+          }
+        }
         // Dequantization of the next B operand (step u+1 of group g, or step 0 of group
         // g+1), spread over the step's MFMAs: masks, then four pairs.
         {
@@ -361,6 +424,12 @@ struct MmTile4 {
             anext = affine(t);
           }
           if (mb == (MB > 1 ? S_MASK : 0)) {
+            // First use of group g+1's codes: redistribute them (a pair starts at an
+            // even group).
+            if (u == 3) {
+              if constexpr (WS && BITS == 4 && I % 2 == 1) wswap(wn.q[0], wr[(I + 2) % PD].q[0]);
+              if constexpr (WS && BITS == 8) wswap(wn.q[0], wn.q[1]);
+            }
             masks(src, un, m);
 #pragma unroll
             for (int e = 0; e < 4; ++e) asm volatile("" : "+v"(m[e]));

@@ -50,13 +50,14 @@ hipError_t launch_tiles(QmmParams p, hipStream_t stream) {
 // biases are staged in LDS once (4-byte copies of its contiguous block) instead of
 // being fetched per group: at M = 600, K = 5120 that is the difference between 110 and
 // 92 us. At 320 rows the activation buffers and the staging area fill the 160 KB.
+// Weights come in 16-row x 64-byte loads (WS), four groups ahead (93 against 95 us).
 template <int BITS, int MB>
 hipError_t launch_mb(QmmParams p, hipStream_t stream) {
   const int G = p.K / p.group;  // scale values per weight row
   const bool stage = G <= 80 && G % 2 == 0 && (reinterpret_cast<uintptr_t>(p.s) & 3) == 0 &&
                      (reinterpret_cast<uintptr_t>(p.b) & 3) == 0;
-  return stage ? launch_tiles<MmTile4<BITS, MB, 4, 3, 2, 1, 80>>(p, stream)
-               : launch_tiles<MmTile4<BITS, MB, 4>>(p, stream);
+  return stage ? launch_tiles<MmTile4<BITS, MB, 4, 4, 2, 1, 80, false, true>>(p, stream)
+               : launch_tiles<MmTile4<BITS, MB, 4, 4, 2, 0, 0, false, true>>(p, stream);
 }
 
 template <int BITS>

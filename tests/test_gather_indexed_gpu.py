@@ -152,3 +152,21 @@ def test_indexed_deterministic():
     for _ in range(5):
         again, _ = run(g, "f32")
         assert np.array_equal(first, again)
+
+
+@pytest.mark.parametrize("tokens", [573, 46])
+@pytest.mark.parametrize("which", ["up", "down"])
+def test_moe_prefill_indexed_sampled(which, tokens):
+    """The benchmark's indexed MoE prefill workloads as timed (routing order; up through
+    the token index): the 573-token prompt and the 46-token one below the grouped path's
+    gate (about three rows per expert). Sampled outputs against the oracle, and the rows
+    equal the sorted gather's rows of the same routing bit for bit."""
+    gi = I.moe_prefill_indexed(which, tokens=tokens)
+    got, flag = run(gi, "bf16")
+    assert flag == 0
+    r, c = G.sample_points(gi.B, gi.N, 400, seed=tokens)
+    G.assert_close(got[r, c], ref(gi, rows=r, cols=c), "bf16", gi.name)
+    gs = I.moe_gather(which, tokens=tokens)
+    ys, _ = G.run_gather(gs, "bf16")
+    order = np.argsort(gs.token_of_row.astype(np.int64) * (gs.E + 1) + gs.expert_idx, kind="stable")
+    assert np.array_equal(got, G.to_f64(ys)[order])
