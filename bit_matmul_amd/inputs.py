@@ -103,8 +103,8 @@ def bf16_bits_to_f64(bits) -> np.ndarray:
 def pack_codes(q, bits: int) -> np.ndarray:
     """Pack unsigned codes [..., K] into uint32 words [..., K*bits//32], LSB first."""
     q = np.asarray(q)
-    if bits not in (4, 8):
-        raise ValueError("bits must be 4 or 8")
+    if bits not in (2, 4, 8):
+        raise ValueError("bits must be 2, 4 or 8")
     per = 32 // bits
     if q.shape[-1] % per:
         raise ValueError("K must be a multiple of 32/bits")

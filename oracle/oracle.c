@@ -10,7 +10,9 @@
  * quantized with 4-bit codes in groups of 64 and every other tensor in bf16;
  * its kernel table names the code type (CUTLASS 4-bit sub-byte integers), and
  * issue #1538 ("Volta (sm_70) baseline record and build coverage", comment of
- * 2026-08-31) sets those against 8-bit unsigned-char codes. So:
+ * 2026-08-31) sets those against 8-bit unsigned-char codes. 2-bit codes, the
+ * narrowest width of the same affine format, are packed the same way (16 per
+ * word). So:
  *
  *   for each output row r and column n
  *     y[r][n] = sum_k x[r][k] * (s[n][g] * q[n][k] + b[n][g]),  g = floor(k / group)
@@ -271,7 +273,7 @@ static int run(const problem_t* p, int nthreads) {
 }
 
 static int check_args(int64_t N, int64_t K, int bits, int group) {
-  if (bits != 4 && bits != 8) return -1;
+  if (bits != 2 && bits != 4 && bits != 8) return -1;
   if (group <= 0 || K <= 0 || N < 0 || K % group != 0 || (K * bits) % 32 != 0) return -1;
   return 0;
 }

@@ -36,6 +36,9 @@ def numpy_codes(w: np.ndarray, bits: int) -> np.ndarray:
     by = np.ascontiguousarray(w).view(np.uint8)  # byte j of word i = bits [8j, 8j+8)
     if bits == 8:
         return by.astype(np.int64)
+    if bits == 2:           # k = 4*byte + i in bits [2i, 2i+2) of the byte
+        parts = [(by >> (2 * i)) & 0x03 for i in range(4)]
+        return np.stack(parts, axis=-1).reshape(*by.shape[:-1], by.shape[-1] * 4).astype(np.int64)
     lo = by & 0x0F          # k = 2*byte
     hi = by >> 4            # k = 2*byte + 1
     return np.stack([lo, hi], axis=-1).reshape(*by.shape[:-1], by.shape[-1] * 2).astype(np.int64)
@@ -132,7 +135,7 @@ def check_unpack_golden(O):
             got = O.code(np.array([word], dtype=np.uint32), k, bits)
             assert got == c, f"bits={bits} word={word:#010x} k={k}: {got} != {c}"
     # multi-word rows: element k lives in word k // (32/bits)
-    for bits in (4, 8):
+    for bits in (2, 4, 8):
         per = 32 // bits
         q = (np.arange(5 * per) * 7 + 3) % (1 << bits)
         row = I.pack_codes(q, bits)
@@ -144,7 +147,7 @@ def check_weight_definition(O):
     """w = s*q + b with the group of k; exact for bf16 s, b (checked in Fractions)."""
     from fractions import Fraction
     rng = np.random.default_rng(5)
-    for bits in (4, 8):
+    for bits in (2, 4, 8):
         K = 256
         q = rng.integers(0, 1 << bits, size=K)
         row = I.pack_codes(q, bits)
@@ -159,7 +162,7 @@ def check_weight_definition(O):
 
 def check_brute_force(O):
     """Tiny shapes: oracle == numpy byte-view unpack + float64 matmul."""
-    for bits in (4, 8):
+    for bits in (2, 4, 8):
         for M in (1, 2, 3, 5):
             for N in (1, 3, 8, 17):
                 for K in (64, 128, 192):
@@ -174,7 +177,7 @@ def check_brute_force_groups(O):
     """Groups of 32 and 128 along K: oracle == numpy (byte-view unpack, scales and
     biases repeated over their group, float64 matmul), dense and indexed gather."""
     for group in (32, 128):
-        for bits in (4, 8):
+        for bits in (2, 4, 8):
             for M, N, K in ((1, 5, 128), (3, 8, 256), (2, 17, 384)):
                 d = I.random_dense(M, N, K, bits, seed=M * 100 + N + K + group, group=group)
                 ref = numpy_qmm(d.x, d.w, d.scales, d.biases, bits, group)
@@ -207,7 +210,7 @@ def integer_exact_problem(M, N, K, bits, seed):
 
 
 def check_integer_exact(O):
-    for bits in (4, 8):
+    for bits in (2, 4, 8):
         for (M, N, K) in ((3, 17, 192), (1, 40, 640), (9, 5, 5120)):
             x, w, s, b, y4 = integer_exact_problem(M, N, K, bits, seed=K + bits)
             got = O.qmm(x, w, s, b, bits)
@@ -236,7 +239,7 @@ def check_closed_form(O):
     """x = 1, q = c everywhere: y[n] = 64 * sum_g (c*s[n,g] + b[n,g])."""
     from fractions import Fraction
     rng = np.random.default_rng(3)
-    for bits in (4, 8):
+    for bits in (2, 4, 8):
         K, N = 320, 6
         for c in (0, 1, (1 << bits) - 1):
             w = I.pack_codes(np.full((N, K), c), bits)
@@ -254,7 +257,7 @@ def check_closed_form(O):
 
 def check_bias_linearity(O):
     """y(b) - y(0) = sum_g b[n,g] * X_g with X_g the group sums of x."""
-    for bits in (4, 8):
+    for bits in (2, 4, 8):
         d = I.random_dense(4, 9, 256, bits, seed=21)
         zero = np.zeros_like(d.biases)
         y1 = O.qmm(d.x, d.w, d.scales, d.biases, bits)
@@ -272,7 +275,7 @@ def check_constant_per_expert(O):
     E, N, K = len(counts), 11, 192
     idx = np.repeat(np.arange(E, dtype=np.int32), counts)
     B = idx.size
-    for bits in (4, 8):
+    for bits in (2, 4, 8):
         w = np.zeros((E, N, K * bits // 32), dtype=np.uint32)
         s = I.to_bf16_bits(np.full((E, N, K // 64), 0.5))
         b = I.to_bf16_bits(np.broadcast_to((np.arange(E) + 1.0)[:, None, None], (E, N, K // 64)))
@@ -297,7 +300,7 @@ def check_invalid_expert_rows(O):
 def check_gather_consistency(O):
     """Per-expert slices of gather_qmm equal qmm on that expert's rows and
     weights; E = 1 equals qmm; permuting rows within a segment permutes outputs."""
-    for bits in (4, 8):
+    for bits in (2, 4, 8):
         g = I.random_gather([4, 0, 7, 2, 5], N=13, K=192, bits=bits, seed=bits)
         y = O.gather_qmm(g.x, g.w, g.scales, g.biases, g.expert_idx, bits)
         for e in range(g.E):
@@ -317,16 +320,21 @@ def check_gather_consistency(O):
 
 
 def check_repack_8bit(O):
-    """Codes below 16 stored as 8-bit give the same result as stored as 4-bit."""
+    """Codes below 16 stored as 8-bit give the same result as stored as 4-bit, and codes
+    below 4 the same again stored as 2-bit."""
     rng = np.random.default_rng(9)
     N, K, M = 7, 192, 3
-    q = rng.integers(0, 16, size=(N, K))
     s = I.random_scales(rng, (N, K // 64))
     b = I.to_bf16_bits(rng.uniform(-0.2, 0.2, size=(N, K // 64)))
     x = I.to_bf16_bits(rng.standard_normal((M, K)))
+    q = rng.integers(0, 16, size=(N, K))
     y4 = O.qmm(x, I.pack_codes(q, 4), s, b, 4)
     y8 = O.qmm(x, I.pack_codes(q, 8), s, b, 8)
     assert np.array_equal(y4, y8)
+    q = rng.integers(0, 4, size=(N, K))
+    y2 = O.qmm(x, I.pack_codes(q, 2), s, b, 2)
+    assert np.array_equal(y2, O.qmm(x, I.pack_codes(q, 4), s, b, 4))
+    assert np.array_equal(y2, O.qmm(x, I.pack_codes(q, 8), s, b, 8))
 
 
 def check_points_and_threads(O):
@@ -362,7 +370,7 @@ def check_indexed_brute_force(O):
     """The indexed gather (row r reads x[token_idx[r]] and expert expert_idx[r], any
     order) against numpy: rows gathered by fancy indexing, each expert dequantized
     densely with the byte-view unpacker, float64 matmul."""
-    for bits in (4, 8):
+    for bits in (2, 4, 8):
         for T, B, E, N, K in ((1, 8, 16, 9, 128), (3, 7, 5, 17, 192), (6, 20, 4, 3, 64)):
             x, w, s, b, tok, exp = _indexed_problem(T, B, E, N, K, bits, seed=T * 100 + B + bits)
             got = O.gather_qmm_indexed(x, w, s, b, tok, exp, bits)
@@ -384,7 +392,7 @@ def check_indexed_constant(O):
     T, E, N, K = 9, 6, 5, 128
     tok = np.array([3, 0, 8, 8, 1, 5, 2, 7, 4, 6, 0, 9, -1, 2], dtype=np.int32)
     exp = np.array([5, 0, 2, 2, 4, 1, 3, 0, 5, 1, 4, 1, 2, 6], dtype=np.int32)
-    for bits in (4, 8):
+    for bits in (2, 4, 8):
         w = np.zeros((E, N, K * bits // 32), dtype=np.uint32)
         s = I.to_bf16_bits(np.full((E, N, K // 64), 0.5))
         b = I.to_bf16_bits(np.broadcast_to((np.arange(E) + 1.0)[:, None, None], (E, N, K // 64)))
