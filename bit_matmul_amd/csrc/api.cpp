@@ -45,12 +45,15 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 // Quantization groups along K the kernels take (each 16-byte chunk of codes lies in one).
 bool group_ok(int g) { return g == 32 || g == 64 || g == 128; }
 
+// Code widths: 4 and 8 bits with any group; 2 bits (64 codes per 16-byte chunk) with
+// groups of 64 and 128.
+bool bits_ok(int bits, int group) { return bits == 4 || bits == 8 || (bits == 2 && group != 32); }
+
 // Shared by qmv / qmm. Sets *empty when there is nothing to compute.
 bitmm_status validate_dense(const void* x, const uint32_t* w, const void* s, const void* b,
                             const void* y, int64_t M, int64_t N, int64_t K, int bits, int group,
                             bitmm_out out, bool* empty) {
-  if (bits != 4 && bits != 8) return BITMM_ERR_UNSUPPORTED;
-  if (!group_ok(group)) return BITMM_ERR_UNSUPPORTED;
+  if (!group_ok(group) || !bits_ok(bits, group)) return BITMM_ERR_UNSUPPORTED;
   if (out != BITMM_OUT_BF16 && out != BITMM_OUT_F32) return BITMM_ERR_UNSUPPORTED;
   if (M < 0 || N < 0 || K < 1 || K % group != 0 || K % 64 != 0) return BITMM_ERR_SHAPE;
   // Index arithmetic inside the kernels is 32-bit per dimension.
@@ -75,7 +78,7 @@ const char* bitmm_status_string(bitmm_status s) {
     case BITMM_OK: return "ok";
     case BITMM_ERR_NULL: return "a required pointer is NULL";
     case BITMM_ERR_SHAPE: return "invalid shape";
-    case BITMM_ERR_UNSUPPORTED: return "unsupported bits, group size or output type";
+    case BITMM_ERR_UNSUPPORTED: return "unsupported bits, group size, type, layout or size";
     case BITMM_ERR_ALIGN: return "misaligned pointer";
     case BITMM_ERR_WORKSPACE: return "workspace missing or too small";
     case BITMM_ERR_DEVICE: return "no HIP device, or the current device is not gfx950";
@@ -138,8 +141,7 @@ bitmm_status bitmm_gather_qmm(const void* x, const uint32_t* w, const void* scal
                               bitmm_out out, void* workspace, size_t workspace_bytes,
                               void* stream) {
   try {
-    if (bits != 4 && bits != 8) return BITMM_ERR_UNSUPPORTED;
-    if (!group_ok(group_size)) return BITMM_ERR_UNSUPPORTED;
+    if (!group_ok(group_size) || !bits_ok(bits, group_size)) return BITMM_ERR_UNSUPPORTED;
     if (out != BITMM_OUT_BF16 && out != BITMM_OUT_F32) return BITMM_ERR_UNSUPPORTED;
     if (B < 0 || N < 0 || K < 1 || E < 1 || K % group_size != 0 || K % 64 != 0) return BITMM_ERR_SHAPE;
     if (B > INT32_MAX || N > INT32_MAX || K > INT32_MAX || E > INT32_MAX - 2)
@@ -177,8 +179,7 @@ bitmm_status bitmm_gather_qmm_indexed(const void* x, const uint32_t* w, const vo
                                       bitmm_out out, void* workspace, size_t workspace_bytes,
                                       void* stream) {
   try {
-    if (bits != 4 && bits != 8) return BITMM_ERR_UNSUPPORTED;
-    if (!group_ok(group_size)) return BITMM_ERR_UNSUPPORTED;
+    if (!group_ok(group_size) || !bits_ok(bits, group_size)) return BITMM_ERR_UNSUPPORTED;
     if (out != BITMM_OUT_BF16 && out != BITMM_OUT_F32) return BITMM_ERR_UNSUPPORTED;
     if (B < 0 || N < 0 || T < 0 || K < 1 || E < 1 || K % group_size != 0 || K % 64 != 0) return BITMM_ERR_SHAPE;
     if (B > INT32_MAX || N > INT32_MAX || K > INT32_MAX || T > INT32_MAX || E > INT32_MAX - 2)
@@ -213,8 +214,7 @@ bitmm_status bitmm_gather_qmv(const void* x, const uint32_t* w, const void* scal
                               int64_t E, int64_t T, int bits, int group_size, bitmm_out out,
                               void* stream) {
   try {
-    if (bits != 4 && bits != 8) return BITMM_ERR_UNSUPPORTED;
-    if (!group_ok(group_size)) return BITMM_ERR_UNSUPPORTED;
+    if (!group_ok(group_size) || !bits_ok(bits, group_size)) return BITMM_ERR_UNSUPPORTED;
     if (out != BITMM_OUT_BF16 && out != BITMM_OUT_F32) return BITMM_ERR_UNSUPPORTED;
     if (B < 0 || N < 0 || T < 0 || K < 1 || E < 1 || K % group_size != 0 || K % 64 != 0) return BITMM_ERR_SHAPE;
     if (B > INT32_MAX || N > INT32_MAX || K > INT32_MAX || E > INT32_MAX || T > INT32_MAX)

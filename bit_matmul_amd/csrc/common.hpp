@@ -14,6 +14,7 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 // 128-bit streaming load (non-temporal hint: the weights are read once).
 __device__ __forceinline__ u32x4_t load_stream(const uint32_t* p) {
@@ -49,6 +50,17 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
 // v_perm_b32: byte i of the result is byte sel[i] of the 8-byte value {hi:lo}.
 __device__ __forceinline__ uint32_t perm_b32(uint32_t hi, uint32_t lo, uint32_t sel) {
   return __builtin_amdgcn_perm(hi, lo, sel);
+}
+
+// 2-bit codes k = 0..7 in bits [2k, 2k+2) of half h of a word, spread to nibbles: code k
+// in bits [4k, 4k+2) of the result (a 4-bit code word holding the same values).
+// One byte permute (bytes 0 and 1 of the half to bytes 0 and 2, zeros between), then
+// two shift-or-mask steps.
+__device__ __forceinline__ uint32_t spread_2bit(uint32_t w, int h) {
+  uint32_t x = __builtin_amdgcn_perm(0u, w, h ? 0x0c030c02u : 0x0c010c00u);
+  x = (x | (x << 4)) & 0x0F0F0F0Fu;
+  x = (x | (x << 2)) & 0x33333333u;
+  return x;
 }
 
 // v_and_or_b32 (a & m) | c. Written out because gfx9 VOP3 encodings take no

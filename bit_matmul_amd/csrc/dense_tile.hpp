@@ -32,7 +32,6 @@ namespace bitmm {
 
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 template <int DT, int LAYOUT, int MB, int KS = 128, int NS = 3>
 struct MmTileD {

@@ -246,8 +246,9 @@ hipError_t launch_grouped(GatherParams p, hipStream_t stream) {
 
 // Scales and biases staged in LDS once per workgroup when the wave's block fits (G <= 48),
 // with 4-byte copies when G is even and both arrays 4-byte aligned. Weights in
-// 16-row x 64-byte loads (WS), four groups ahead: 1-5 % faster than 32 x 32-byte loads
-// three groups ahead on the MoE shapes.
+// 16-row x 64-byte loads (WS; 2-bit codes load their 8 bytes per lane directly), four
+// groups ahead: 1-5 % faster than 32 x 32-byte loads three groups ahead on the MoE
+// shapes.
 template <int BITS, typename T, bool RMAP>
 hipError_t launch_form(GatherParams p, hipStream_t stream) {
   if constexpr (RMAP)
@@ -262,12 +263,12 @@ hipError_t launch_sb(GatherParams p, hipStream_t stream) {
   const bool wide = G % 2 == 0 && (reinterpret_cast<uintptr_t>(p.s) & 3) == 0 &&
                     (reinterpret_cast<uintptr_t>(p.b) & 3) == 0;
   if (G <= 12)
-    return wide ? launch_form<BITS, MmTile4<BITS, MB, 4, 4, 2, 1, 12, RMAP, true>, RMAP>(p, stream)
-                : launch_form<BITS, MmTile4<BITS, MB, 4, 4, 2, 2, 12, RMAP, true>, RMAP>(p, stream);
+    return wide ? launch_form<BITS, MmTile4<BITS, MB, 4, 4, 2, 1, 12, RMAP, BITS != 2>, RMAP>(p, stream)
+                : launch_form<BITS, MmTile4<BITS, MB, 4, 4, 2, 2, 12, RMAP, BITS != 2>, RMAP>(p, stream);
   if (G <= 48)
-    return wide ? launch_form<BITS, MmTile4<BITS, MB, 4, 4, 2, 1, 48, RMAP, true>, RMAP>(p, stream)
-                : launch_form<BITS, MmTile4<BITS, MB, 4, 4, 2, 2, 48, RMAP, true>, RMAP>(p, stream);
-  return launch_form<BITS, MmTile4<BITS, MB, 4, 4, 2, 0, 0, RMAP, true>, RMAP>(p, stream);
+    return wide ? launch_form<BITS, MmTile4<BITS, MB, 4, 4, 2, 1, 48, RMAP, BITS != 2>, RMAP>(p, stream)
+                : launch_form<BITS, MmTile4<BITS, MB, 4, 4, 2, 2, 48, RMAP, BITS != 2>, RMAP>(p, stream);
+  return launch_form<BITS, MmTile4<BITS, MB, 4, 4, 2, 0, 0, RMAP, BITS != 2>, RMAP>(p, stream);
 }
 
 // One row of 4 waves, each with 32 weight rows: every expert's weights are dequantized
@@ -314,7 +315,9 @@ hipError_t launch_gather_qmm(const uint16_t* x, const uint32_t* w, const uint16_
   p.group = group;
   p.tiles_n = 0;
   p.out_f32 = out_f32 ? 1 : 0;
-  return bits == 4 ? launch_tile4<4, false>(p, stream) : launch_tile4<8, false>(p, stream);
+  return bits == 4 ? launch_tile4<4, false>(p, stream)
+       : bits == 2 ? launch_tile4<2, false>(p, stream)
+                   : launch_tile4<8, false>(p, stream);
 }
 
 size_t gather_indexed_workspace_bytes(int64_t B, int64_t E) {
@@ -358,7 +361,9 @@ hipError_t launch_gather_qmm_indexed(const uint16_t* x, const uint32_t* w, const
   p.group = group;
   p.tiles_n = 0;
   p.out_f32 = out_f32 ? 1 : 0;
-  return bits == 4 ? launch_tile4<4, true>(p, stream) : launch_tile4<8, true>(p, stream);
+  return bits == 4 ? launch_tile4<4, true>(p, stream)
+       : bits == 2 ? launch_tile4<2, true>(p, stream)
+                   : launch_tile4<8, true>(p, stream);
 }
 
 }  // namespace bitmm

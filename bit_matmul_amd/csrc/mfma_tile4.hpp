@@ -70,12 +70,13 @@ struct MmTile4 {
   static constexpr int LDS_BYTES = NB * XB + SB_BYTES;
   static constexpr int XI = BM / 8;              // 1 KB copies per group
   static constexpr int XC = XI / WAVES;          // copies per wave per group
-  static constexpr int WV = BITS / 4;            // 16-byte code loads per lane per group
+  static constexpr int WV = BITS == 8 ? 2 : 1;   // code loads per lane per group (16 B; 8 B at 2 bits)
   static constexpr int GB = 8 * BITS;            // bytes of one group of codes (32 WV)
   static constexpr int WL = WV + (SBM == 0 ? 2 : 0);  // weight-side loads per group
   static constexpr int NP = 4 * MB;              // MFMAs per group
   static constexpr int PF = 4;                   // activation reads in flight
-  static_assert(BITS == 4 || BITS == 8, "bits");
+  static_assert(BITS == 2 || BITS == 4 || BITS == 8, "bits");
+  static_assert(!WS || BITS != 2, "2-bit codes load 8 bytes per lane");
   static_assert(SBM >= 0 && SBM <= 2 && (SBM == 0) == (GMAX == 0), "scale/bias staging");
   static_assert(XI % WAVES == 0, "every wave issues the same number of copies");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
@@ -168,7 +169,7 @@ struct MmTile4 {
         xoff[k] = (uint32_t)(tr * K * 2 + dma_chunk(I, lane) * 16);
       }
     }
-    const uint32_t woff = (uint32_t)(lc * rowbytes + lh * 16 * WV);
+    const uint32_t woff = (uint32_t)(lc * rowbytes + lh * 4 * BITS);  // codes 32h .. 32h+31
     // WS: lane (m, q) = (lane % 16, lane / 16) loads chunk c(q) of a 64-byte span of row m
     // (first instruction) and of row 16 + m (second); c(q) = q at 8 bits (the span is one
     // group) and 0, 2, 1, 3 at 4 bits (two groups: the swap must leave chunk h of each
@@ -190,6 +191,9 @@ struct MmTile4 {
       if constexpr (WS && BITS == 8) {
         r.q[0] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rw, wsx, gc * GB, 0));
         r.q[1] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rw, wsy, gc * GB, 0));
+      } else if constexpr (BITS == 2) {
+        const u32x2_t v = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rw, woff, gc * GB, 0));
+        r.q[0] = u32x4_t{v[0], v[1], 0u, 0u};
       } else {
 #pragma unroll
         for (int v = 0; v < WV; ++v)
@@ -245,7 +249,7 @@ struct MmTile4 {
       a.s = __uint_as_float(r.s << 16);
       const float b = __uint_as_float(r.b << 16);
       a.b0 = fmaf(-1024.f, a.s, b);
-      if constexpr (BITS == 4) {
+      if constexpr (BITS <= 4) {
         a.s16 = a.s * 0.0625f;
         a.b1 = fmaf(-64.f, a.s, b);
       } else {
@@ -255,11 +259,12 @@ struct MmTile4 {
       return a;
     };
     // Packed f16 code registers for k-step u: 4-bit (q0,q4) (16q1,16q5) (q2,q6)
-    // (16q3,16q7); 8-bit (q0,q2) (q1,q3) (q4,q6) (q5,q7).
+    // (16q3,16q7); 8-bit (q0,q2) (q1,q3) (q4,q6) (q5,q7). 2-bit codes 8u .. 8u+7 of the
+    // lane are spread to a nibble word first and then taken as 4-bit.
     auto masks = [&](const Wraw& r, int u, uint32_t (&m)[4]) {
       const uint32_t magic = 0x64006400u;  // f16 pair (1024, 1024)
-      if constexpr (BITS == 4) {
-        const uint32_t wd = r.q[0][u];
+      if constexpr (BITS <= 4) {
+        const uint32_t wd = BITS == 4 ? r.q[0][u] : spread_2bit(r.q[0][u >> 1], u & 1);
         const uint32_t w8 = wd >> 8;
         m[0] = and_or_b32(wd, 0x000F000Fu, magic);
         m[1] = and_or_b32(wd, 0x00F000F0u, magic);
@@ -277,7 +282,7 @@ struct MmTile4 {
     // bf16 pair e (k-slots 2e, 2e+1 of the lane's 8) of a B operand.
     auto pair = [&](const Aff& a, const uint32_t (&m)[4], int e) -> uint32_t {
       float lo, hi;
-      if constexpr (BITS == 4) {
+      if constexpr (BITS <= 4) {
         // (w0,w1) low halves of m0,m1; (w2,w3) low of m2,m3; (w4,w5), (w6,w7) high halves
         const uint32_t p0 = m[2 * (e & 1)], p1 = m[2 * (e & 1) + 1];
         if (e < 2) {

@@ -56,8 +56,8 @@ hipError_t launch_mb(QmmParams p, hipStream_t stream) {
   const int G = p.K / p.group;  // scale values per weight row
   const bool stage = G <= 80 && G % 2 == 0 && (reinterpret_cast<uintptr_t>(p.s) & 3) == 0 &&
                      (reinterpret_cast<uintptr_t>(p.b) & 3) == 0;
-  return stage ? launch_tiles<MmTile4<BITS, MB, 4, 4, 2, 1, 80, false, true>>(p, stream)
-               : launch_tiles<MmTile4<BITS, MB, 4, 4, 2, 0, 0, false, true>>(p, stream);
+  return stage ? launch_tiles<MmTile4<BITS, MB, 4, 4, 2, 1, 80, false, BITS != 2>>(p, stream)
+               : launch_tiles<MmTile4<BITS, MB, 4, 4, 2, 0, 0, false, BITS != 2>>(p, stream);
 }
 
 template <int BITS>
@@ -90,7 +90,9 @@ hipError_t launch_qmm_mfma(const uint16_t* x, const uint32_t* w, const uint16_t*
   p.group = group;
   p.out_f32 = out_f32 ? 1 : 0;
   p.tiles_m = p.tiles_n = 0;
-  return bits == 4 ? launch_tile4<4>(p, stream) : launch_tile4<8>(p, stream);
+  return bits == 4 ? launch_tile4<4>(p, stream)
+       : bits == 2 ? launch_tile4<2>(p, stream)
+                   : launch_tile4<8>(p, stream);
 }
 
 }  // namespace bitmm

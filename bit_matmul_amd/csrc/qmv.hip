@@ -5,7 +5,8 @@
 //     waves of a workgroup (K <= 16384 at 4 bits and 8192 at 8 bits for up to 3 rows,
 //     half that from 4 rows), the small-M prefill tail;
 //   qmv_kernel (qmv_impl.hpp): up to 8 activation rows per launch, any K (several
-//     passes over K when a row does not fit), for what the other two do not take.
+//     passes over K when a row does not fit), for what the other two do not take, and
+//     for 2-bit codes (four rows per launch).
 #include <stdlib.h>
 
 #include <atomic>
@@ -59,7 +60,9 @@ hipError_t launch_rows(const uint16_t* x, const uint32_t* w, const uint16_t* sca
                        int group, bool out_f32, const GemvBatch& bt, hipStream_t stream) {
   const int64_t nch = K * bits / 128;  // 16-byte code chunks per weight row
   const size_t ysz = out_f32 ? 4 : 2;
-  if (M == 1 && forced_path() == 0 && qmv_dma_detail::pick_lanes(nch) != 0) {
+  // 2-bit codes run the general kernel only (rows four at a time: a chunk carries 64
+  // activations per row).
+  if (M == 1 && bits != 2 && forced_path() == 0 && qmv_dma_detail::pick_lanes(nch) != 0) {
     qmv_dma_detail::Params dp;
     dp.x = x;
     dp.w = w;
@@ -77,7 +80,7 @@ hipError_t launch_rows(const uint16_t* x, const uint32_t* w, const uint16_t* sca
     return bits == 4 ? qmv_dma_detail::launch_bits<4>(dp, compute_units(), wpc, stream)
                      : qmv_dma_detail::launch_bits<8>(dp, compute_units(), wpc, stream);
   }
-  if (forced_path() == 0 && M <= 8 && qmv_split_detail::fits(K, bits, M)) {
+  if (forced_path() == 0 && bits != 2 && M <= 8 && qmv_split_detail::fits(K, bits, M)) {
     qmv_split_detail::Params sp;
     sp.x = x;
     sp.w = w;
@@ -92,11 +95,13 @@ hipError_t launch_rows(const uint16_t* x, const uint32_t* w, const uint16_t* sca
     return bits == 4 ? qmv_split_detail::launch_bits<4>(sp, (int)M, stream)
                      : qmv_split_detail::launch_bits<8>(sp, (int)M, stream);
   }
-  for (int64_t m0 = 0; m0 < M; m0 += 8) {
-    const int mr = (int)(M - m0 < 8 ? M - m0 : 8);
+  const int rows_per_launch = bits == 2 ? 4 : 8;
+  for (int64_t m0 = 0; m0 < M; m0 += rows_per_launch) {
+    const int mr = (int)(M - m0 < rows_per_launch ? M - m0 : rows_per_launch);
     // Chunks per lane per pass over K: as few passes as possible, with at most
-    // 4 chunks, and at most 12 chunk-rows of activations held per lane.
-    const int64_t cap = mr <= 3 ? 4 : (12 / mr > 0 ? 12 / mr : 1);
+    // 4 chunks, and at most 12 chunk-rows of activations held per lane (at 2 bits,
+    // where a chunk has twice the activations, 2 chunks for one row and 1 beyond).
+    const int64_t cap = bits == 2 ? (mr == 1 ? 2 : 1) : (mr <= 3 ? 4 : (12 / mr > 0 ? 12 / mr : 1));
     const int64_t passes = (nch + cap * kWave - 1) / (cap * kWave);
     const int cpl = (int)((nch + passes * kWave - 1) / (passes * kWave));
     qmv_detail::QmvParams p;
@@ -110,8 +115,9 @@ hipError_t launch_rows(const uint16_t* x, const uint32_t* w, const uint16_t* sca
     p.gshift = group_shift(group);
     p.out_f32 = out_f32 ? 1 : 0;
     p.bt = bt;
-    const hipError_t e = bits == 4 ? qmv_detail::launch_bits<4>(p, mr, cpl, stream)
-                                   : qmv_detail::launch_bits<8>(p, mr, cpl, stream);
+    const hipError_t e = bits == 4   ? qmv_detail::launch_bits<4>(p, mr, cpl, stream)
+                         : bits == 2 ? qmv_detail::launch_bits<2>(p, mr, cpl, stream)
+                                     : qmv_detail::launch_bits<8>(p, mr, cpl, stream);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

@@ -12,7 +12,8 @@
 //     sum_k x_k (s q_k + b) = s * sum_k x_k q_k + b * sum_k x_k.
 // 4-bit: a masked nibble pair OR 0x4300 is the bf16 pair (128+q_i, 128+q_{i+4}),
 // exact, so v_dot2_f32_bf16 against the matching activation pair gives
-// P = sum x (128 + q) with exact products; then s*P + (b - 128 s)*sum x.
+// P = sum x (128 + q) with exact products; then s*P + (b - 128 s)*sum x. 2-bit: each
+// 16-bit half of a code word is spread to a nibble word first, then as 4-bit.
 // 8-bit: codes convert to f32 one byte at a time and multiply f32 activations.
 // Every product is exact in f32; accumulation is f32 (the pages' decode fix,
 // epic #1536 diagnosis item 3: accumulate the 4-bit GEMV in float, not bf16).
@@ -118,15 +119,18 @@ __global__ __launch_bounds__(kQmvThreads) void qmv_kernel(QmvParams p) {
 #pragma unroll
         for (int u = 0; u < XU; ++u)
           if (!ok[i]) xr[i][m][u] = u32x4_t{0u, 0u, 0u, 0u};
-      if constexpr (BITS == 4) {
-        // Activation pairs matching the nibble pairs (j, j+4) of each word.
-        uint32_t xp[MR][4][4];
+      if constexpr (BITS == 4 || BITS == 2) {
+        // Nibble words of 8 codes each (2-bit codes are spread to nibbles first, so
+        // both widths share the arithmetic). Activation pairs matching the nibble
+        // pairs (j, j+4) of each word.
+        constexpr int NWD = 16 / BITS;
+        uint32_t xp[MR][NWD][4];
         float sx[MR];
 #pragma unroll
         for (int m = 0; m < MR; ++m) {
           float t = 0.f;
 #pragma unroll
-          for (int wd = 0; wd < 4; ++wd) {
+          for (int wd = 0; wd < NWD; ++wd) {
             const u32x4_t d = xr[i][m][wd];
             xp[m][wd][0] = perm_b32(d[2], d[0], 0x05040100u);  // (x0, x4)
             xp[m][wd][1] = perm_b32(d[2], d[0], 0x07060302u);  // (x1, x5)
@@ -144,8 +148,8 @@ __global__ __launch_bounds__(kQmvThreads) void qmv_kernel(QmvParams p) {
 #pragma unroll
           for (int m = 0; m < MR; ++m) P[m] = 0.f;
 #pragma unroll
-          for (int wd = 0; wd < 4; ++wd) {
-            const uint32_t w0 = q[i][r][wd];
+          for (int wd = 0; wd < NWD; ++wd) {
+            const uint32_t w0 = BITS == 4 ? q[i][r][wd] : spread_2bit(q[i][r][wd >> 1], wd & 1);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
               // bf16 pair (128 + q_j, 128 + q_{j+4}), exact.
@@ -236,18 +240,30 @@ hipError_t pick_rpw(const QmvParams& p, hipStream_t stream) {
   return launch_one<BITS, MR, RPW, CPL>(p, stream);
 }
 
+// At most 4 chunks per lane; at 2 bits (64 activations per chunk and row) 2 for one
+// row and 1 beyond (the host chooses cpl within that).
 template <int BITS, int MR>
 hipError_t pick_cpl(const QmvParams& p, int cpl, hipStream_t stream) {
-  switch (cpl) {
-    case 1: return pick_rpw<BITS, MR, 1>(p, stream);
-    case 2: return pick_rpw<BITS, MR, 2>(p, stream);
-    case 3: return pick_rpw<BITS, MR, 3>(p, stream);
-    default: return pick_rpw<BITS, MR, 4>(p, stream);
-  }
+  constexpr int CMAX = BITS == 2 ? (MR == 1 ? 2 : 1) : 4;
+  if (cpl <= 1 || CMAX == 1) return pick_rpw<BITS, MR, 1>(p, stream);
+  if constexpr (CMAX >= 2)
+    if (cpl == 2 || CMAX == 2) return pick_rpw<BITS, MR, 2>(p, stream);
+  if constexpr (CMAX >= 3)
+    if (cpl == 3 || CMAX == 3) return pick_rpw<BITS, MR, 3>(p, stream);
+  if constexpr (CMAX >= 4) return pick_rpw<BITS, MR, 4>(p, stream);
+  return hipErrorInvalidValue;
 }
 
 template <int BITS>
 hipError_t launch_bits(const QmvParams& p, int mr, int cpl, hipStream_t stream) {
+  if constexpr (BITS == 2) {  // four rows per launch at 2 bits
+    switch (mr) {
+      case 1: return pick_cpl<BITS, 1>(p, cpl, stream);
+      case 2: return pick_cpl<BITS, 2>(p, cpl, stream);
+      case 3: return pick_cpl<BITS, 3>(p, cpl, stream);
+      default: return pick_cpl<BITS, 4>(p, cpl, stream);
+    }
+  } else {
   switch (mr) {
     case 1: return pick_cpl<BITS, 1>(p, cpl, stream);
     case 2: return pick_cpl<BITS, 2>(p, cpl, stream);
@@ -258,11 +274,13 @@ hipError_t launch_bits(const QmvParams& p, int mr, int cpl, hipStream_t stream) 
     case 7: return pick_cpl<BITS, 7>(p, cpl, stream);
     default: return pick_cpl<BITS, 8>(p, cpl, stream);
   }
+  }
 }
 
 }  // namespace qmv_detail
 
 // One explicit instantiation per bit width, each in its own translation unit.
+extern template hipError_t qmv_detail::launch_bits<2>(const qmv_detail::QmvParams&, int, int, hipStream_t);
 extern template hipError_t qmv_detail::launch_bits<4>(const qmv_detail::QmvParams&, int, int, hipStream_t);
 extern template hipError_t qmv_detail::launch_bits<8>(const qmv_detail::QmvParams&, int, int, hipStream_t);
 

@@ -7,7 +7,8 @@
  * the decode GEMV (second row). Its Baseline section describes the weights as
  * affine quantized, 4-bit codes in groups of 64, with every other tensor in bf16;
  * issue #1538 ("Volta (sm_70) baseline record and build coverage", comments of
- * 2026-08-31) adds 8-bit codes. PR #1562 ("tag the pre-Ampere grouped GEMM arm
+ * 2026-08-31) adds 8-bit codes; 2-bit codes, the narrowest width of the same format,
+ * are packed by the same rule. PR #1562 ("tag the pre-Ampere grouped GEMM arm
  * Sm70, not Sm75", section "The branch is live") adds the third form: the
  * quantized GatherQMM that a MoE prefill runs over rows sorted by expert. All
  * three compute
@@ -33,6 +34,7 @@
  * epic's sub-issue list, is to stop accumulating the 4-bit GEMV in bf16).
  *   - bitmm_qmv, and bitmm_qmm for M < 8: every product x*w is formed exactly (the
  *     code enters as an exact bf16 integer and the group scale is applied in f32).
+ *     2-bit codes take the general GEMV kernel, four activation rows per launch.
  *   - bitmm_qmm for M >= 8 and bitmm_gather_qmm: w = fma(s, q, b) in f32 is rounded
  *     to bf16 and multiplied on the matrix cores (a dense bf16 GEMM after
  *     dequantization, as the grouped path on the pages is), f32 accumulate.
@@ -65,7 +67,8 @@ typedef enum {
   BITMM_ERR_NULL = 1,        /* a required pointer is NULL                                  */
   BITMM_ERR_SHAPE = 2,       /* M, N, B < 0; K < 1; E < 1; K not a multiple of 64 and of
                                 group_size                                                  */
-  BITMM_ERR_UNSUPPORTED = 3, /* bits not in {4, 8}; group_size not in {32, 64, 128}; unknown
+  BITMM_ERR_UNSUPPORTED = 3, /* bits not in {2, 4, 8}; group_size not in {32, 64, 128}, or 32
+                                with 2-bit codes; unknown
                                 output type, operand type or layout; a size limit stated
                                 at the entry point                                          */
   BITMM_ERR_ALIGN = 4,       /* x, w or workspace not 16-byte aligned; scales or biases not
@@ -98,7 +101,8 @@ const char* bitmm_status_string(bitmm_status s);
  * rows (rows are taken eight at a time). Meant for M = 1 (the decode step the epic's
  * kernel table lists second); any M >= 0 is accepted.
  *   x: bf16 [M, K]; w: uint32 [N, K*bits/32]; scales, biases: bf16 [N, K/group_size];
- *   y: [M, N] of type `out`. bits in {4, 8}; group_size in {32, 64, 128} (the epic's
+ *   y: [M, N] of type `out`. bits in {2, 4, 8}; group_size in {32, 64, 128} (64 or 128
+ *   at 2 bits, where one 16-byte chunk holds 64 codes; the epic's
  *   checkpoint is group 64; its diagnosis item 4 quotes a tile rule keyed on
  *   group_size <= 64, so other group sizes exist in the format); K a multiple of 64 and
  *   of group_size.

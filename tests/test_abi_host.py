@@ -85,7 +85,9 @@ def dense_args(**kw):
 
 DENSE_CASES = [
     (dict(bits=3), bm.BITMM_ERR_UNSUPPORTED),
-    (dict(bits=2), bm.BITMM_ERR_UNSUPPORTED),
+    (dict(bits=2, group=32), bm.BITMM_ERR_UNSUPPORTED),  # 2 bits: groups of 64 and 128
+    (dict(bits=1), bm.BITMM_ERR_UNSUPPORTED),
+    (dict(bits=16), bm.BITMM_ERR_UNSUPPORTED),
     (dict(group=16), bm.BITMM_ERR_UNSUPPORTED),
     (dict(group=256), bm.BITMM_ERR_UNSUPPORTED),
     (dict(group=48), bm.BITMM_ERR_UNSUPPORTED),
@@ -131,9 +133,11 @@ def test_dense_valid_without_device(L):
     if gpu_present():
         pytest.skip("fake pointers would reach a real device")
     for fn in (L.bitmm_qmv, L.bitmm_qmm):
-        for bits in (4, 8):
+        for bits in (2, 4, 8):
             for M in (1, 3, 8, 600):
                 for group in (32, 64, 128):
+                    if bits == 2 and group == 32:
+                        continue
                     assert fn(*dense_args(bits=bits, M=M, out=1, group=group)) == bm.BITMM_ERR_DEVICE
 
 
@@ -150,6 +154,8 @@ def gather_args(**kw):
 
 GATHER_CASES = [
     (dict(bits=5), bm.BITMM_ERR_UNSUPPORTED),
+    (dict(bits=2, group=32), bm.BITMM_ERR_UNSUPPORTED),
+    (dict(bits=2, group=128), None),
     (dict(group=16), bm.BITMM_ERR_UNSUPPORTED),
     (dict(out=-1), bm.BITMM_ERR_UNSUPPORTED),
     (dict(E=0), bm.BITMM_ERR_SHAPE),
@@ -188,7 +194,9 @@ def gqmv_args(**kw):
 
 
 GQMV_CASES = [
-    (dict(bits=2), bm.BITMM_ERR_UNSUPPORTED),
+    (dict(bits=2, group=32), bm.BITMM_ERR_UNSUPPORTED),  # 2 bits: groups of 64 and 128
+    (dict(bits=1), bm.BITMM_ERR_UNSUPPORTED),
+    (dict(bits=16), bm.BITMM_ERR_UNSUPPORTED),
     (dict(group=256), bm.BITMM_ERR_UNSUPPORTED),
     (dict(out=7), bm.BITMM_ERR_UNSUPPORTED),
     (dict(K=704, group=128), bm.BITMM_ERR_SHAPE),
@@ -238,6 +246,8 @@ def gidx_args(**kw):
 
 GIDX_CASES = [
     (dict(bits=3), bm.BITMM_ERR_UNSUPPORTED),
+    (dict(bits=2, group=32), bm.BITMM_ERR_UNSUPPORTED),
+    (dict(bits=2), None),
     (dict(group=16), bm.BITMM_ERR_UNSUPPORTED),
     (dict(out=2), bm.BITMM_ERR_UNSUPPORTED),
     (dict(E=8193), bm.BITMM_ERR_UNSUPPORTED),
