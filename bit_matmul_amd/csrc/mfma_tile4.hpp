@@ -81,10 +81,18 @@ struct MmTile4 {
   static_assert(XI % WAVES == 0, "every wave issues the same number of copies");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
   static_assert(PD >= 2 && XD >= 1 && XD <= PD, "prefetch depths");
-  static_assert(!WS || BITS == 8 || (PD % 2 == 0 && XD == 2), "paired weight loads");
-  // Loads issued after the copies of group g+1, when body g waits for them: the weight
-  // loads of that body and the copies and weight loads of the XD-1 bodies after it.
-  static constexpr int VM_AFTER_COPY = WL + (XD - 1) * (XC + WL);
+  static_assert(!WS || BITS == 8 || PD % 2 == 0, "paired weight loads");
+  // Weight-side loads issued by body h: WL each, or with paired 4-bit loads 2 WL from odd
+  // bodies and none from even ones (only h's parity matters; h may be negative).
+  static constexpr int loads_of(int h) { return (WS && BITS == 4) ? ((h & 1) ? 2 * WL : 0) : WL; }
+  // Body g (slot I, same parity) waits for the copies of group g+1, issued at steps 0-2 of
+  // body g+1-XD: after them come that body's weight loads, then the copies and weight
+  // loads of the XD-1 bodies up to g.
+  static constexpr int vm_after_copy(int I) {
+    int t = (XD - 1) * XC;
+    for (int d = 0; d < XD; ++d) t += loads_of(I - d);
+    return t;
+  }
   static_assert(PD * WL + XD * XC <= 63, "vmcnt range");
   static_assert(WAVES * BM * 64 <= NB * XB, "epilogue staging fits in the activation buffers");
 
@@ -455,7 +463,7 @@ struct MmTile4 {
       acur = anext;
       // The copies of group g+1 (issued XD-1 bodies earlier) and everything before them
       // have landed; later copies and weight loads may still fly.
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(VM_AFTER_COPY) : "memory");
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(vm_after_copy(I)) : "memory");
       barrier_no_fence();
     };
 
