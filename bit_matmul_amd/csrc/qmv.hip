@@ -1,12 +1,12 @@
 // Host side of the GEMV / small-M path. Three kernel forms:
 //   qmv_dma_kernel (qmv_dma.hpp): one activation row, K up to 5 chunks per lane
-//     (K <= 10240 at 4 bits, <= 5120 at 8 bits), the decode GEMV;
+//     (K <= 10240 at 4 bits, <= 5120 at 8 bits, <= 20480 at 2 bits), the decode GEMV;
 //   qmv_split_kernel (qmv_split.hpp): up to 8 activation rows with K split across the
 //     waves of a workgroup (K <= 16384 at 4 bits and 8192 at 8 bits for up to 3 rows,
 //     half that from 4 rows), the small-M prefill tail;
 //   qmv_kernel (qmv_impl.hpp): up to 8 activation rows per launch, any K (several
 //     passes over K when a row does not fit), for what the other two do not take, and
-//     for 2-bit codes (four rows per launch).
+//     for 2-bit codes with several rows (four rows per launch).
 #include <stdlib.h>
 
 #include <atomic>
@@ -60,9 +60,9 @@ hipError_t launch_rows(const uint16_t* x, const uint32_t* w, const uint16_t* sca
                        int group, bool out_f32, const GemvBatch& bt, hipStream_t stream) {
   const int64_t nch = K * bits / 128;  // 16-byte code chunks per weight row
   const size_t ysz = out_f32 ? 4 : 2;
-  // 2-bit codes run the general kernel only (rows four at a time: a chunk carries 64
-  // activations per row).
-  if (M == 1 && bits != 2 && forced_path() == 0 && qmv_dma_detail::pick_lanes(nch) != 0) {
+  // 2-bit codes: the decode kernel for one row, else the general kernel (rows four at a
+  // time: a chunk carries 64 activations per row).
+  if (M == 1 && forced_path() == 0 && qmv_dma_detail::pick_lanes(nch) != 0) {
     qmv_dma_detail::Params dp;
     dp.x = x;
     dp.w = w;
@@ -77,8 +77,9 @@ hipError_t launch_rows(const uint16_t* x, const uint32_t* w, const uint16_t* sca
     dp.bt = bt;
     // BITMM_QMV_WAVES_PER_CU: launch-shape tuning knob (0 = the built-in target).
     const int wpc = env_int("BITMM_QMV_WAVES_PER_CU");
-    return bits == 4 ? qmv_dma_detail::launch_bits<4>(dp, compute_units(), wpc, stream)
-                     : qmv_dma_detail::launch_bits<8>(dp, compute_units(), wpc, stream);
+    return bits == 4   ? qmv_dma_detail::launch_bits<4>(dp, compute_units(), wpc, stream)
+           : bits == 2 ? qmv_dma_detail::launch_bits<2>(dp, compute_units(), wpc, stream)
+                       : qmv_dma_detail::launch_bits<8>(dp, compute_units(), wpc, stream);
   }
   if (forced_path() == 0 && bits != 2 && M <= 8 && qmv_split_detail::fits(K, bits, M)) {
     qmv_split_detail::Params sp;

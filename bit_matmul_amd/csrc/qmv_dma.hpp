@@ -18,7 +18,9 @@
 //   sum_k x_k (s q_k + b) = s * sum_k x_k q_k + b * sum_k x_k.
 // 4-bit: a nibble pair masked into 0x4300 is the exact bf16 pair (128+q_j, 128+q_{j+4});
 // v_dot2_f32_bf16 against the matching activation pair gives P = sum x (128 + q),
-// then s*P + (b - 128 s) * sum x. 8-bit: codes convert to f32 byte by byte.
+// then s*P + (b - 128 s) * sum x. 8-bit: codes convert to f32 byte by byte. 2-bit: the
+// code pair (j, j+8) of a word masked into 0x4300 is the bf16 pair (128+q_j, 128+q_{j+8})
+// (the activation pairs come from LDS at each step: a 64-code chunk has 32 of them).
 // Products are exact in f32 and accumulation is f32 (the decode fix of epic #1536,
 // diagnosis item 3: accumulate the 4-bit GEMV in float).
 #pragma once
@@ -57,9 +59,11 @@ struct Cfg {
   static constexpr int D = SPW <= 2 ? SPW + 1 : (SPW < 5 ? SPW : 5);
   static constexpr int XCH = 64 * C;     // activation chunks held in LDS (covers L * C)
   // Activations per chunk in LDS: 4-bit 16 bf16 pairs matched to nibble pairs (64 B);
-  // 8-bit 16 f32 (64 B). Stored as 4 planes of 16 bytes, plane u of chunk c at
-  // (u * XCH + c) * 16, so the 64 lanes' reads of one plane are contiguous.
-  static constexpr int X_BYTES = 4 * XCH * 16;
+  // 8-bit 16 f32 (64 B); 2-bit 32 pairs (128 B, a chunk holds 64 codes). Stored as NPL
+  // planes of 16 bytes, plane u of chunk c at (u * XCH + c) * 16, so the 64 lanes' reads
+  // of one plane are contiguous.
+  static constexpr int NPL = BITS == 2 ? 8 : 4;
+  static constexpr int X_BYTES = NPL * XCH * 16;
   static constexpr int LDS_BYTES = X_BYTES + XCH * 4;  // + per-chunk activation sums
 };
 
@@ -128,7 +132,7 @@ __global__ __launch_bounds__(kThreads) void qmv_dma_kernel(Params p) {
   // registers for the whole kernel. Their loads are issued first, so waiting for
   // them never waits for weight loads (loads retire in order).
   constexpr int XPT = (T::XCH + kThreads - 1) / kThreads;  // chunks per thread
-  constexpr int XU = BITS == 4 ? 4 : 2;                     // 16-byte activation loads per chunk
+  constexpr int XU = T::CC / 8;                             // 16-byte activation loads per chunk
   u32x4_t xin[XPT][XU];
 #pragma unroll
   for (int j = 0; j < XPT; ++j) {
@@ -152,7 +156,7 @@ __global__ __launch_bounds__(kThreads) void qmv_dma_kernel(Params p) {
     const int c = threadIdx.x + j * kThreads;
     if (c >= T::XCH) break;
     const bool ok = c < nch;
-    uint32_t raw[BITS == 4 ? 16 : 8];
+    uint32_t raw[4 * XU];
 #pragma unroll
     for (int u = 0; u < XU; ++u)
 #pragma unroll
@@ -161,8 +165,16 @@ __global__ __launch_bounds__(kThreads) void qmv_dma_kernel(Params p) {
 #pragma unroll
     for (int d = 0; d < 4 * XU; ++d) t = dot2_bf16(raw[d], 0x3F803F80u, t);
     reinterpret_cast<float*>(lds + T::X_BYTES)[c] = t;
-    uint32_t out[16];
-    if constexpr (BITS == 4) {
+    uint32_t out[4 * T::NPL];
+    if constexpr (BITS == 2) {
+      // code word d holds codes 16 d .. 16 d + 15; the 2-bit pair (j, j+8) meets the
+      // activation pair (x_{16d+j}, x_{16d+j+8}), stored as out[8 d + j].
+#pragma unroll
+      for (int d = 0; d < 4; ++d)
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          out[8 * d + j] = perm_b32(raw[8 * d + 4 + j / 2], raw[8 * d + j / 2], (j & 1) ? 0x07060302u : 0x05040100u);
+    } else if constexpr (BITS == 4) {
       // code word wd holds codes 8 wd .. 8 wd + 7; nibble pair (j, j+4) meets the
       // activation pair (x_{8wd+j}, x_{8wd+j+4}).
 #pragma unroll
@@ -181,19 +193,24 @@ __global__ __launch_bounds__(kThreads) void qmv_dma_kernel(Params p) {
       }
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+    for (int u = 0; u < T::NPL; ++u)
       *reinterpret_cast<u32x4_t*>(lds + (u * T::XCH + c) * 16) =
           u32x4_t{out[4 * u], out[4 * u + 1], out[4 * u + 2], out[4 * u + 3]};
   }
   __syncthreads();
   if (!active) return;
-  u32x4_t xr[C][4];
+  // The lane's activation pairs stay in registers (2-bit: 32 per chunk, read from LDS
+  // at each step instead).
+  constexpr int XRP = BITS == 2 ? 1 : 4;
+  u32x4_t xr[C][XRP];
   float sx[C];
 #pragma unroll
   for (int m = 0; m < C; ++m) {
     const int c = li + L * m;
+    if constexpr (BITS != 2) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) xr[m][u] = *reinterpret_cast<const u32x4_t*>(lds + (u * T::XCH + c) * 16);
+      for (int u = 0; u < 4; ++u) xr[m][u] = *reinterpret_cast<const u32x4_t*>(lds + (u * T::XCH + c) * 16);
+    }
     sx[m] = reinterpret_cast<const float*>(lds + T::X_BYTES)[c];
   }
 
@@ -205,7 +222,22 @@ __global__ __launch_bounds__(kThreads) void qmv_dma_kernel(Params p) {
       const float s = __uint_as_float(S.s[m] << 16);
       const float b = __uint_as_float(S.b[m] << 16);
       float P[4] = {0.f, 0.f, 0.f, 0.f};
-      if constexpr (BITS == 4) {
+      if constexpr (BITS == 2) {
+        // 2-bit pair (j, j+8) of code word d masked into 0x4300: the exact bf16 pair
+        // (128 + q_j, 128 + q_{j+8}), against activation pair 8 d + j (planes 2d, 2d+1).
+        const int c = li + L * m;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          const u32x4_t x0 = *reinterpret_cast<const u32x4_t*>(lds + ((2 * d) * T::XCH + c) * 16);
+          const u32x4_t x1 = *reinterpret_cast<const u32x4_t*>(lds + ((2 * d + 1) * T::XCH + c) * 16);
+          const uint32_t wd = S.q[m][d];
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            P[j & 3] = dot2_bf16(and_or_b32(wd >> (2 * j), 0x00030003u, magic), j < 4 ? x0[j] : x1[j - 4], P[j & 3]);
+        }
+        const float Pt = (P[0] + P[1]) + (P[2] + P[3]);
+        acc = fmaf(s, Pt, fmaf(fmaf(-128.f, s, b), sx[m], acc));
+      } else if constexpr (BITS == 4) {
 #pragma unroll
         for (int wd = 0; wd < 4; ++wd)
 #pragma unroll
@@ -308,6 +340,7 @@ hipError_t launch_bits(const Params& p, int cus, int wpc, hipStream_t stream) {
 
 }  // namespace qmv_dma_detail
 
+extern template hipError_t qmv_dma_detail::launch_bits<2>(const qmv_dma_detail::Params&, int, int, hipStream_t);
 extern template hipError_t qmv_dma_detail::launch_bits<4>(const qmv_dma_detail::Params&, int, int, hipStream_t);
 extern template hipError_t qmv_dma_detail::launch_bits<8>(const qmv_dma_detail::Params&, int, int, hipStream_t);
 

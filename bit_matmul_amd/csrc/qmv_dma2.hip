@@ -1,0 +1,6 @@
+// 2-bit instantiations of the decode GEMV.
+#include "qmv_dma.hpp"
+
+namespace bitmm {
+template hipError_t qmv_dma_detail::launch_bits<2>(const qmv_dma_detail::Params&, int, int, hipStream_t);
+}  // namespace bitmm

@@ -1,4 +1,4 @@
-// 8-bit instantiations of the LDS-ring GEMV.
+// 8-bit instantiations of the decode GEMV.
 #include "qmv_dma.hpp"
 
 namespace bitmm {
