@@ -23,7 +23,8 @@ the MoE expert-gathered GEMM in both orientations, sorted and in routing order t
 the indexed entry point, also at a 46-token prompt below the grouped path's gate, the
 MoE decode step's gathered GEMV at 1 and 4 tokens in both orientations, and the dense
 grouped product of a non-quantized MoE layer, bf16, both orientations and both weight
-layouts), timed the same way.
+layouts, and the format variants: the decode GEMV with 2-bit codes and with groups of
+128, the prefill GEMM with groups of 32), timed the same way.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-suite] [--no-cpu]
                        [--calibrate-copy]
@@ -141,18 +142,19 @@ class Case:
         ts, y, ws = self.sets[self.i % self.copies]
         self.i += 1
         bm, p = self.bm, self.p
+        gs = getattr(p, "group", 64)
         if self.kind == "qmv":
-            bm.bitmm_qmv(*ts, y, p.bits)
+            bm.bitmm_qmv(*ts, y, p.bits, group_size=gs)
         elif self.kind == "qmm":
-            bm.bitmm_qmm(*ts, y, p.bits)
+            bm.bitmm_qmm(*ts, y, p.bits, group_size=gs)
         elif self.kind == "gather_qmv":
-            bm.bitmm_gather_qmv(*ts, *self.ids, y, p.bits)
+            bm.bitmm_gather_qmv(*ts, *self.ids, y, p.bits, group_size=gs)
         elif self.kind == "gather_indexed":
-            bm.bitmm_gather_qmm_indexed(*ts, *self.ids, y, ws, p.bits)
+            bm.bitmm_gather_qmm_indexed(*ts, *self.ids, y, ws, p.bits, group_size=gs)
         elif self.kind == "gather_mm":
             bm.bitmm_gather_mm(*ts, *self.ids, y, ws, p.layout)
         else:
-            bm.bitmm_gather_qmm(*ts, y, ws, p.bits)
+            bm.bitmm_gather_qmm(*ts, y, ws, p.bits, group_size=gs)
 
 
 def time_steps(torch, cases, steps, warmup):
@@ -317,7 +319,10 @@ def main():
                  ("gather_indexed", lambda: I.moe_prefill_indexed("up", tokens=46)),
                  ("gather_indexed", lambda: I.moe_prefill_indexed("down", tokens=46)),
                  ("gather_mm", lambda: I.moe_gather_mm("up")), ("gather_mm", lambda: I.moe_gather_mm("down")),
-                 ("gather_mm", lambda: I.moe_gather_mm("up", layout="kn"))]
+                 ("gather_mm", lambda: I.moe_gather_mm("up", layout="kn")),
+                 ("qmv", lambda: I.random_dense(1, 13824, 5120, 2, seed=1)),
+                 ("qmv", lambda: I.random_dense(1, 13824, 5120, 4, seed=1, group=128)),
+                 ("qmm", lambda: I.random_dense(600, 13824, 5120, 4, seed=1, group=32))]
         for kind, make in specs:
             p = make()
             c = Case(torch, p, kind, torch.bfloat16)

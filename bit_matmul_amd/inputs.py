@@ -461,7 +461,8 @@ def random_dense(M: int, N: int, K: int, bits: int, seed: int = 0, x_dist: str =
     rx = rng_for(seed, TAG_X, 7, M, N, K)
     xf = rx.standard_normal(size=(M, K)) if x_dist == "normal" else rx.uniform(-1, 1, size=(M, K))
     w, s, b = _dense_weights(seed, N, K, bits, sub=7, group=group)
-    return Dense(f"dense_M{M}_K{K}_N{N}_b{bits}", to_bf16_bits(xf), w, s, b, bits, group)
+    gname = "" if group == GROUP else f"_g{group}"
+    return Dense(f"dense_M{M}_K{K}_N{N}_b{bits}{gname}", to_bf16_bits(xf), w, s, b, bits, group)
 
 
 def random_gather(counts, N: int, K: int, bits: int, seed: int = 0, group: int = GROUP) -> Gather:
