@@ -80,6 +80,18 @@ def test_qmv_dma_layouts(N, K, bits, out, monkeypatch):
     G.assert_close(got, oracle_dense(d), out, f"qmv[dma] N{N} K{K} b{bits}")
 
 
+@pytest.mark.parametrize("bits", [2, 4, 8])
+@pytest.mark.parametrize("wpc", [1, 4, 8])
+def test_qmv_dma_steps_per_wave(wpc, bits, monkeypatch):
+    """The decode kernel with several steps per wave (the launch target set low: 8, 4 or 2
+    consecutive steps per wave, straight-line code with up to four steps in flight),
+    including a ragged last wave."""
+    monkeypatch.setenv("BITMM_QMV_WAVES_PER_CU", str(wpc))
+    d = I.random_dense(1, 4099 * 2 + 1, 1024, bits, seed=wpc + bits)
+    got = G.to_f64(G.run_dense("bitmm_qmv", d, "f32"))
+    G.assert_close(got, oracle_dense(d), "f32", f"qmv[dma] wpc{wpc} b{bits}")
+
+
 @pytest.mark.parametrize("bits", [4, 8])
 @pytest.mark.parametrize("out", ["bf16", "f32"])
 @pytest.mark.parametrize("M,N,K", [(1, 130, 320), (2, 64, 128), (3, 200, 640), (5, 33, 192),
