@@ -264,8 +264,8 @@ def main():
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": read_traffic("qmv_K5120_N13824_b4_traffic", src_hash),
-                "kernel": "qmv_dma_kernel<4, 32, 5, *> (K=5120, N=13824, 4-bit, M=1: steps of "
-                          "2 rows x 32 lanes x 5 chunks)",
+                "kernel": "qmv_dma_kernel<4, 64, 3, 1> (K=5120, N=13824, 4-bit, M=1: one step of "
+                          "1 row x 64 lanes x 3 chunks per wave)",
                 "algorithmic_bytes_per_launch": cb.bytes,
                 "avg_launch_us": round(tb * 1e6, 3)}
 
@@ -321,7 +321,8 @@ def main():
                  ("gather_mm", lambda: I.moe_gather_mm("up")), ("gather_mm", lambda: I.moe_gather_mm("down")),
                  ("gather_mm", lambda: I.moe_gather_mm("up", layout="kn")),
                  ("qmv", lambda: I.random_dense(1, 13824, 5120, 2, seed=1)),
-                 ("qmv", lambda: I.random_dense(1, 13824, 5120, 4, seed=1, group=128)),
+                 # 13952 rows rather than 13824: a grid of its own in kernel traces
+                 ("qmv", lambda: I.random_dense(1, 13952, 5120, 4, seed=1, group=128)),
                  ("qmm", lambda: I.random_dense(600, 13824, 5120, 4, seed=1, group=32))]
         for kind, make in specs:
             p = make()
