@@ -132,19 +132,24 @@ __global__ __launch_bounds__(kThreads) void qmv_dma_kernel(Params p) {
     for (int m = 0; m < C; ++m) S.b[m] = __builtin_amdgcn_raw_buffer_load_b16(rb, soff[m], 0, 0);
   };
 
-  // Activations, once per workgroup: thread t prepares chunks t, t + 256, ... (zero
-  // past the row end) into LDS; each lane then copies its own C chunks into
-  // registers for the whole kernel. Their loads are issued first, so waiting for
-  // them never waits for weight loads (loads retire in order).
+  // Activations, once per workgroup: thread t prepares chunks t, t + 256, ... into
+  // LDS; each lane then copies its own C chunks into registers for the whole kernel.
+  // The loads go through a descriptor over the row, so chunks past its end read as
+  // zeros with no per-word select (N = 13824, K = 5120: 11.1 -> 10.1 us). They are
+  // issued first, so waiting for them never waits for weight loads (loads retire in
+  // order).
   constexpr int XPT = (T::XCH + kThreads - 1) / kThreads;  // chunks per thread
   constexpr int XU = T::CC / 8;                             // 16-byte activation loads per chunk
   u32x4_t xin[XPT][XU];
+  {
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(uniform_ptr(xq), (int64_t)K * 2);
 #pragma unroll
-  for (int j = 0; j < XPT; ++j) {
-    const int c = threadIdx.x + j * kThreads;
-    const bool ok = c < nch;
+    for (int j = 0; j < XPT; ++j) {
+      const uint32_t c = threadIdx.x + j * kThreads;
 #pragma unroll
-    for (int u = 0; u < XU; ++u) xin[j][u] = load_u128(xq + (int64_t)(ok ? c : 0) * T::CC + 8 * u);
+      for (int u = 0; u < XU; ++u)
+        xin[j][u] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rx, c * (T::CC * 2) + 16 * u, 0, 0));
+    }
   }
 
   __builtin_amdgcn_sched_barrier(0);  // activation loads first: they retire first
@@ -160,12 +165,11 @@ __global__ __launch_bounds__(kThreads) void qmv_dma_kernel(Params p) {
   for (int j = 0; j < XPT; ++j) {
     const int c = threadIdx.x + j * kThreads;
     if (c >= T::XCH) break;
-    const bool ok = c < nch;
     uint32_t raw[4 * XU];
 #pragma unroll
     for (int u = 0; u < XU; ++u)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) raw[4 * u + e] = ok ? xin[j][u][e] : 0u;
+      for (int e = 0; e < 4; ++e) raw[4 * u + e] = xin[j][u][e];
     float t = 0.f;
 #pragma unroll
     for (int d = 0; d < 4 * XU; ++d) t = dot2_bf16(raw[d], 0x3F803F80u, t);
