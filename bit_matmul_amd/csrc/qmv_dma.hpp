@@ -230,7 +230,9 @@ __global__ __launch_bounds__(kThreads) void qmv_dma_kernel(Params p) {
     for (int m = 0; m < C; ++m) {
       const float s = __uint_as_float(S.s[m] << 16);
       const float b = __uint_as_float(S.b[m] << 16);
-      float P[4] = {0.f, 0.f, 0.f, 0.f};
+      // One accumulator per chunk: the chains of the C chunks and of the other waves
+      // hide the latency, and no partial sums are left to add (N = 5120: 5.72 -> 5.62 us).
+      float P = 0.f;
       if constexpr (BITS == 2) {
         // 2-bit pair (j, j+8) of code word d masked into 0x4300: the exact bf16 pair
         // (128 + q_j, 128 + q_{j+8}), against activation pair 8 d + j (planes 2d, 2d+1).
@@ -242,26 +244,23 @@ __global__ __launch_bounds__(kThreads) void qmv_dma_kernel(Params p) {
           const uint32_t wd = S.q[m][d];
 #pragma unroll
           for (int j = 0; j < 8; ++j)
-            P[j & 3] = dot2_bf16(and_or_b32(wd >> (2 * j), 0x00030003u, magic), j < 4 ? x0[j] : x1[j - 4], P[j & 3]);
+            P = dot2_bf16(and_or_b32(wd >> (2 * j), 0x00030003u, magic), j < 4 ? x0[j] : x1[j - 4], P);
         }
-        const float Pt = (P[0] + P[1]) + (P[2] + P[3]);
-        acc = fmaf(s, Pt, fmaf(fmaf(-128.f, s, b), sx[m], acc));
+        acc = fmaf(s, P, fmaf(fmaf(-128.f, s, b), sx[m], acc));
       } else if constexpr (BITS == 4) {
 #pragma unroll
         for (int wd = 0; wd < 4; ++wd)
 #pragma unroll
           for (int j = 0; j < 4; ++j)
-            P[j] = dot2_bf16(and_or_b32(S.q[m][wd] >> (4 * j), 0x000F000Fu, magic), xr[m][wd][j], P[j]);
-        const float Pt = (P[0] + P[1]) + (P[2] + P[3]);
-        acc = fmaf(s, Pt, fmaf(fmaf(-128.f, s, b), sx[m], acc));
+            P = dot2_bf16(and_or_b32(S.q[m][wd] >> (4 * j), 0x000F000Fu, magic), xr[m][wd][j], P);
+        acc = fmaf(s, P, fmaf(fmaf(-128.f, s, b), sx[m], acc));
       } else {
 #pragma unroll
         for (int wd = 0; wd < 4; ++wd)
 #pragma unroll
           for (int j = 0; j < 4; ++j)
-            P[j] = fmaf(__uint_as_float(xr[m][wd][j]), (float)((S.q[m][wd] >> (8 * j)) & 0xFFu), P[j]);
-        const float Pt = (P[0] + P[1]) + (P[2] + P[3]);
-        acc = fmaf(s, Pt, fmaf(b, sx[m], acc));
+            P = fmaf(__uint_as_float(xr[m][wd][j]), (float)((S.q[m][wd] >> (8 * j)) & 0xFFu), P);
+        acc = fmaf(s, P, fmaf(b, sx[m], acc));
       }
     }
     const float v = lane_group_sum<L>(acc);
