@@ -44,11 +44,14 @@ struct Params {
 
 constexpr uint32_t kNoChunk = 0x80000000u;   // outside every descriptor: reads zeros
 
-// Launch shape per row count: blocks of 2 two-row steps (measured best at K = 5120); up to 3 rows, up to 16 waves
-// (1024 threads, at most 128 registers per lane); from 4 rows the activations need more
-// registers, so up to 8 waves (256 registers).
+// Launch shape per row count: up to 3 rows, up to 16 waves (1024 threads, at most 128
+// registers per lane); from 4 rows the activations need more registers, so up to 8
+// waves (256 registers). Blocks of 2 two-row steps, 3 for three rows at 8 bits
+// (measured at K = 5120, N = 13824: 8-bit M = 3 27.1 -> 24.2 us with 3; 8-bit M = 2 20.3 ->
+// 23.2 and 4-bit M = 3 18.0 -> 18.1 with 3, and 4-bit M = 3 or 4 rows slower with 4).
 constexpr int max_waves(int mr) { return mr <= 3 ? 16 : 8; }
-constexpr int steps(int) { return 2; }
+template <int BITS>
+constexpr int steps(int mr) { return BITS == 8 && mr == 3 ? 3 : 2; }
 
 // 16-byte code chunks per weight row, and whether this kernel takes the shape.
 inline int64_t chunks(int64_t K, int bits) { return K * bits / 128; }
@@ -279,7 +282,7 @@ hipError_t launch_s(const Params& p, hipStream_t stream) {
 
 template <int BITS, int MR>
 hipError_t launch_mr(const Params& p, hipStream_t stream) {
-  return launch_s<BITS, MR, steps(MR)>(p, stream);
+  return launch_s<BITS, MR, steps<BITS>(MR)>(p, stream);
 }
 
 // Caller guarantees fits(K, BITS, mr).
