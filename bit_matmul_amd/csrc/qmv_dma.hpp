@@ -19,8 +19,9 @@
 // 4-bit: a nibble pair masked into 0x4300 is the exact bf16 pair (128+q_j, 128+q_{j+4});
 // v_dot2_f32_bf16 against the matching activation pair gives P = sum x (128 + q),
 // then s*P + (b - 128 s) * sum x. 8-bit: codes convert to f32 byte by byte. 2-bit: the
-// code pair (j, j+8) of a word masked into 0x4300 is the bf16 pair (128+q_j, 128+q_{j+8})
-// (the activation pairs come from LDS at each step: a 64-code chunk has 32 of them).
+// code pair (j, j+8) of a word, masked at bit 0, 2 or 4 into the bf16 pair of 128, 32 or
+// 8, is that offset plus (q_j, q_{j+8}) exactly (the activation pairs come from LDS at
+// each step: a 64-code chunk has 32 of them).
 // Products are exact in f32 and accumulation is f32 (the decode fix of epic #1536,
 // diagnosis item 3: accumulate the 4-bit GEMV in float).
 #pragma once
@@ -69,7 +70,9 @@ struct Cfg {
   // of one plane are contiguous.
   static constexpr int NPL = BITS == 2 ? 8 : 4;
   static constexpr int X_BYTES = NPL * XCH * 16;
-  static constexpr int LDS_BYTES = X_BYTES + XCH * 4;  // + per-chunk activation sums
+  // + per-chunk activation sums (2-bit: also the offset term of the chunk, see below)
+  static constexpr int NSUM = BITS == 2 ? 2 : 1;
+  static constexpr int LDS_BYTES = X_BYTES + NSUM * XCH * 4;
 };
 
 // Byte offset outside every descriptor: such a load reads zeros.
@@ -170,20 +173,32 @@ __global__ __launch_bounds__(kThreads) void qmv_dma_kernel(Params p) {
     for (int u = 0; u < XU; ++u)
 #pragma unroll
       for (int e = 0; e < 4; ++e) raw[4 * u + e] = xin[j][u][e];
-    float t = 0.f;
-#pragma unroll
-    for (int d = 0; d < 4 * XU; ++d) t = dot2_bf16(raw[d], 0x3F803F80u, t);
-    reinterpret_cast<float*>(lds + T::X_BYTES)[c] = t;
     uint32_t out[4 * T::NPL];
     if constexpr (BITS == 2) {
       // code word d holds codes 16 d .. 16 d + 15; the 2-bit pair (j, j+8) meets the
-      // activation pair (x_{16d+j}, x_{16d+j+8}), stored as out[8 d + j].
+      // activation pair (x_{16d+j}, x_{16d+j+8}), stored as out[8 d + j]. The pairs of
+      // codes j = 0, 3, 6 are read at offset 128, j = 1, 4, 7 at 32 and j = 2, 5 at 8
+      // (see the arithmetic below): besides the chunk's sum, keep the offset term
+      // 128 sA + 32 sB + 8 sC over those three classes of pairs.
 #pragma unroll
       for (int d = 0; d < 4; ++d)
 #pragma unroll
         for (int j = 0; j < 8; ++j)
           out[8 * d + j] = perm_b32(raw[8 * d + 4 + j / 2], raw[8 * d + j / 2], (j & 1) ? 0x07060302u : 0x05040100u);
-    } else if constexpr (BITS == 4) {
+      float tc[3] = {0.f, 0.f, 0.f};
+#pragma unroll
+      for (int d = 0; d < 4; ++d)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) tc[j % 3] = dot2_bf16(out[8 * d + j], 0x3F803F80u, tc[j % 3]);
+      reinterpret_cast<float*>(lds + T::X_BYTES)[c] = (tc[0] + tc[1]) + tc[2];
+      reinterpret_cast<float*>(lds + T::X_BYTES + T::XCH * 4)[c] = fmaf(128.f, tc[0], fmaf(32.f, tc[1], 8.f * tc[2]));
+    } else {
+      float t = 0.f;
+#pragma unroll
+      for (int d = 0; d < 4 * XU; ++d) t = dot2_bf16(raw[d], 0x3F803F80u, t);
+      reinterpret_cast<float*>(lds + T::X_BYTES)[c] = t;
+    }
+    if constexpr (BITS == 4) {
       // code word wd holds codes 8 wd .. 8 wd + 7; nibble pair (j, j+4) meets the
       // activation pair (x_{8wd+j}, x_{8wd+j+4}).
 #pragma unroll
@@ -194,7 +209,7 @@ __global__ __launch_bounds__(kThreads) void qmv_dma_kernel(Params p) {
         out[4 * wd + 2] = perm_b32(d3, d1, 0x05040100u);
         out[4 * wd + 3] = perm_b32(d3, d1, 0x07060302u);
       }
-    } else {
+    } else if constexpr (BITS == 8) {
 #pragma unroll
       for (int d = 0; d < 8; ++d) {
         out[2 * d] = raw[d] << 16;             // f32 bits of the low bf16
@@ -212,7 +227,7 @@ __global__ __launch_bounds__(kThreads) void qmv_dma_kernel(Params p) {
   // at each step instead).
   constexpr int XRP = BITS == 2 ? 1 : 4;
   u32x4_t xr[C][XRP];
-  float sx[C];
+  float sx[C], ox[C];
 #pragma unroll
   for (int m = 0; m < C; ++m) {
     const int c = li + L * m;
@@ -221,6 +236,7 @@ __global__ __launch_bounds__(kThreads) void qmv_dma_kernel(Params p) {
       for (int u = 0; u < 4; ++u) xr[m][u] = *reinterpret_cast<const u32x4_t*>(lds + (u * T::XCH + c) * 16);
     }
     sx[m] = reinterpret_cast<const float*>(lds + T::X_BYTES)[c];
+    ox[m] = BITS == 2 ? reinterpret_cast<const float*>(lds + T::X_BYTES + (T::NSUM - 1) * T::XCH * 4)[c] : 0.f;
   }
 
   const uint32_t magic = 0x43004300u;  // bf16 pair (128, 128)
@@ -234,19 +250,32 @@ __global__ __launch_bounds__(kThreads) void qmv_dma_kernel(Params p) {
       // hide the latency, and no partial sums are left to add (N = 5120: 5.72 -> 5.62 us).
       float P = 0.f;
       if constexpr (BITS == 2) {
-        // 2-bit pair (j, j+8) of code word d masked into 0x4300: the exact bf16 pair
-        // (128 + q_j, 128 + q_{j+8}), against activation pair 8 d + j (planes 2d, 2d+1).
+        // 2-bit pair (j, j+8) of code word d, against activation pair 8 d + j (planes
+        // 2d, 2d+1). A 2-bit field at bit 0, 2 or 4 of a half, ORed into 0x4300, 0x4200
+        // or 0x4100 (bf16 128, 32, 8: mantissa steps 1, 1/4, 1/16), reads as the exact
+        // bf16 128 + q, 32 + q or 8 + q. So the word, shifted by 0, 6 and 12, gives all
+        // eight pairs with one mask each: codes j = 0, 3, 6 at offset 128, 1, 4, 7 at 32,
+        // 2, 5 at 8, and P = sum x q + (the chunk's offset term ox).
         const int c = li + L * m;
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
           const u32x4_t x0 = *reinterpret_cast<const u32x4_t*>(lds + ((2 * d) * T::XCH + c) * 16);
           const u32x4_t x1 = *reinterpret_cast<const u32x4_t*>(lds + ((2 * d + 1) * T::XCH + c) * 16);
           const uint32_t wd = S.q[m][d];
-#pragma unroll
-          for (int j = 0; j < 8; ++j)
-            P = dot2_bf16(and_or_b32(wd >> (2 * j), 0x00030003u, magic), j < 4 ? x0[j] : x1[j - 4], P);
+          const uint32_t w6 = wd >> 6, w12 = wd >> 12;
+          constexpr uint32_t M0 = 0x00030003u, M2 = 0x000C000Cu, M4 = 0x00300030u;
+          constexpr uint32_t O128 = 0x43004300u, O32 = 0x42004200u, O8 = 0x41004100u;
+          P = dot2_bf16(and_or_b32(wd, M0, O128), x0[0], P);
+          P = dot2_bf16(and_or_b32(wd, M2, O32), x0[1], P);
+          P = dot2_bf16(and_or_b32(wd, M4, O8), x0[2], P);
+          P = dot2_bf16(and_or_b32(w6, M0, O128), x0[3], P);
+          P = dot2_bf16(and_or_b32(w6, M2, O32), x1[0], P);
+          P = dot2_bf16(and_or_b32(w6, M4, O8), x1[1], P);
+          P = dot2_bf16(and_or_b32(w12, M0, O128), x1[2], P);
+          P = dot2_bf16(and_or_b32(w12, M2, O32), x1[3], P);
         }
-        acc = fmaf(s, P, fmaf(fmaf(-128.f, s, b), sx[m], acc));
+        // s (P - ox) + b sum x
+        acc = fmaf(s, P, fmaf(b, sx[m], fmaf(-s, ox[m], acc)));
       } else if constexpr (BITS == 4) {
 #pragma unroll
         for (int wd = 0; wd < 4; ++wd)
