@@ -3,10 +3,10 @@
 //     (K <= 10240 at 4 bits, <= 5120 at 8 bits, <= 20480 at 2 bits), the decode GEMV;
 //   qmv_split_kernel (qmv_split.hpp): up to 8 activation rows with K split across the
 //     waves of a workgroup (K <= 16384 at 4 bits and 8192 at 8 bits for up to 3 rows,
-//     half that from 4 rows), the small-M prefill tail;
+//     half that from 4 rows; 2 bits: up to 3 rows, K <= 16384), the small-M prefill tail;
 //   qmv_kernel (qmv_impl.hpp): up to 8 activation rows per launch, any K (several
-//     passes over K when a row does not fit), for what the other two do not take, and
-//     for 2-bit codes with several rows (four rows per launch).
+//     passes over K when a row does not fit), for what the other two do not take (2-bit
+//     codes with four rows or more: four rows per launch).
 #include <stdlib.h>
 
 #include <atomic>
@@ -60,8 +60,8 @@ hipError_t launch_rows(const uint16_t* x, const uint32_t* w, const uint16_t* sca
                        int group, bool out_f32, const GemvBatch& bt, hipStream_t stream) {
   const int64_t nch = K * bits / 128;  // 16-byte code chunks per weight row
   const size_t ysz = out_f32 ? 4 : 2;
-  // 2-bit codes: the decode kernel for one row, else the general kernel (rows four at a
-  // time: a chunk carries 64 activations per row).
+  // 2-bit codes: the decode kernel for one row, the split-K kernel for up to 3 rows, else
+  // the general kernel (rows four at a time: a chunk carries 64 activations per row).
   if (M == 1 && forced_path() == 0 && qmv_dma_detail::pick_lanes(nch) != 0) {
     qmv_dma_detail::Params dp;
     dp.x = x;
@@ -81,7 +81,7 @@ hipError_t launch_rows(const uint16_t* x, const uint32_t* w, const uint16_t* sca
            : bits == 2 ? qmv_dma_detail::launch_bits<2>(dp, compute_units(), wpc, stream)
                        : qmv_dma_detail::launch_bits<8>(dp, compute_units(), wpc, stream);
   }
-  if (forced_path() == 0 && bits != 2 && M <= 8 && qmv_split_detail::fits(K, bits, M)) {
+  if (forced_path() == 0 && M <= 8 && qmv_split_detail::fits(K, bits, M)) {
     qmv_split_detail::Params sp;
     sp.x = x;
     sp.w = w;
@@ -93,8 +93,9 @@ hipError_t launch_rows(const uint16_t* x, const uint32_t* w, const uint16_t* sca
     sp.gshift = group_shift(group);
     sp.out_f32 = out_f32 ? 1 : 0;
     sp.bt = bt;
-    return bits == 4 ? qmv_split_detail::launch_bits<4>(sp, (int)M, stream)
-                     : qmv_split_detail::launch_bits<8>(sp, (int)M, stream);
+    return bits == 4   ? qmv_split_detail::launch_bits<4>(sp, (int)M, stream)
+           : bits == 2 ? qmv_split_detail::launch_bits<2>(sp, (int)M, stream)
+                       : qmv_split_detail::launch_bits<8>(sp, (int)M, stream);
   }
   const int rows_per_launch = bits == 2 ? 4 : 8;
   for (int64_t m0 = 0; m0 < M; m0 += rows_per_launch) {

@@ -19,7 +19,11 @@
 // 4-bit: a nibble pair masked into 0x4300 is the exact bf16 pair (128 + q_j, 128 + q_{j+4});
 // v_dot2_f32_bf16 against the activation pair (x_j, x_{j+4}) forms P = sum x (128 + q)
 // with exact products, then s P + (b - 128 s) sum x. 8-bit: codes convert to f32 byte by
-// byte. Accumulation is f32 throughout (the decode fix of epic #1536, diagnosis item 3).
+// byte. 2-bit (up to 3 rows): the code pair (j, j+8) of a word, masked at bit 0, 2 or 4
+// into the bf16 pair of 128, 32 or 8, is that offset plus (q_j, q_{j+8}) exactly; P then
+// carries the offset term o = 128 sA + 32 sB + 8 sC of the three classes of activation
+// pairs, and the chunk adds s (P - o) + b sum x. Accumulation is f32 throughout (the
+// decode fix of epic #1536, diagnosis item 3).
 #pragma once
 
 #include <algorithm>
@@ -50,19 +54,22 @@ constexpr uint32_t kNoChunk = 0x80000000u;   // outside every descriptor: reads 
 // (measured at K = 5120, N = 13824: 8-bit M = 3 27.1 -> 24.2 us with 3; 8-bit M = 2 20.3 ->
 // 23.2 and 4-bit M = 3 18.0 -> 18.1 with 3, and 4-bit M = 3 or 4 rows slower with 4).
 constexpr int max_waves(int mr) { return mr <= 3 ? 16 : 8; }
+// 2-bit: 32 activation pairs per row and lane, so up to 3 rows and 8 waves.
+constexpr int max_waves(int mr, int bits) { return bits == 2 ? 8 : max_waves(mr); }
 template <int BITS>
 constexpr int steps(int mr) { return BITS == 8 && mr == 3 ? 3 : 2; }
 
 // 16-byte code chunks per weight row, and whether this kernel takes the shape.
 inline int64_t chunks(int64_t K, int bits) { return K * bits / 128; }
 inline bool fits(int64_t K, int bits, int64_t mr) {
-  return mr >= 1 && mr <= 8 && chunks(K, bits) <= 32 * max_waves((int)mr);
+  return mr >= 1 && mr <= (bits == 2 ? 3 : 8) && chunks(K, bits) <= 32 * max_waves((int)mr, bits);
 }
 
 template <int BITS, int MR, int S, int MAXW>
 __global__ __launch_bounds__(64 * MAXW) void qmv_split_kernel(Params p) {
   constexpr int CC = 128 / BITS;         // codes per chunk
   constexpr int XU = CC / 8;             // 16-byte activation loads per chunk and row
+  constexpr int XV = BITS == 2 ? 32 : 16;  // activation registers per row
   constexpr int RW = 2 * S;              // weight rows per block
   constexpr int NL = 3 * S;              // load instructions per block
   __shared__ float part[2][MAXW * RW * MR];
@@ -140,8 +147,8 @@ __global__ __launch_bounds__(64 * MAXW) void qmv_split_kernel(Params p) {
 
   // 2. Activations of this lane's chunk, per row: the pairs (4-bit) or f32 values
   //    (8-bit) that meet the codes, and their sum.
-  uint32_t xv[MR][16];
-  float sx[MR];
+  uint32_t xv[MR][XV];
+  float sx[MR], ox[MR];
 #pragma unroll
   for (int m = 0; m < MR; ++m) {
     uint32_t raw[4 * XU];
@@ -149,6 +156,23 @@ __global__ __launch_bounds__(64 * MAXW) void qmv_split_kernel(Params p) {
     for (int u = 0; u < XU; ++u)
 #pragma unroll
       for (int e = 0; e < 4; ++e) raw[4 * u + e] = ok ? xin[m][u][e] : 0u;
+    ox[m] = 0.f;
+    if constexpr (BITS == 2) {
+      // code word d holds codes 16 d .. 16 d + 15; the pair (j, j+8) meets the activation
+      // pair (x_{16d+j}, x_{16d+j+8}); classes j = 0, 3, 6 / 1, 4, 7 / 2, 5 (offsets 128,
+      // 32, 8) have their own sums.
+      float tc[3] = {0.f, 0.f, 0.f};
+#pragma unroll
+      for (int d = 0; d < 4; ++d)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          xv[m][8 * d + j] = perm_b32(raw[8 * d + 4 + j / 2], raw[8 * d + j / 2], (j & 1) ? 0x07060302u : 0x05040100u);
+          tc[j % 3] = dot2_bf16(xv[m][8 * d + j], 0x3F803F80u, tc[j % 3]);
+        }
+      sx[m] = (tc[0] + tc[1]) + tc[2];
+      ox[m] = fmaf(128.f, tc[0], fmaf(32.f, tc[1], 8.f * tc[2]));
+      continue;
+    }
     float t = 0.f;
 #pragma unroll
     for (int d = 0; d < 4 * XU; ++d) t = dot2_bf16(raw[d], 0x3F803F80u, t);
@@ -187,7 +211,20 @@ __global__ __launch_bounds__(64 * MAXW) void qmv_split_kernel(Params p) {
       float P[MR];
 #pragma unroll
       for (int m = 0; m < MR; ++m) P[m] = 0.f;
-      if constexpr (BITS == 4) {
+      if constexpr (BITS == 2) {
+        constexpr uint32_t MK[3] = {0x00030003u, 0x000C000Cu, 0x00300030u};
+        constexpr uint32_t OF[3] = {0x43004300u, 0x42004200u, 0x41004100u};
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          const uint32_t wsh[3] = {B.q[i][d], B.q[i][d] >> 6, B.q[i][d] >> 12};
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const uint32_t qp = and_or_b32(wsh[j / 3], MK[j % 3], OF[j % 3]);
+#pragma unroll
+            for (int m = 0; m < MR; ++m) P[m] = dot2_bf16(qp, xv[m][8 * d + j], P[m]);
+          }
+        }
+      } else if constexpr (BITS == 4) {
 #pragma unroll
         for (int wd = 0; wd < 4; ++wd)
 #pragma unroll
@@ -209,7 +246,8 @@ __global__ __launch_bounds__(64 * MAXW) void qmv_split_kernel(Params p) {
       const float cb = BITS == 4 ? fmaf(-128.f, s, b) : b;
 #pragma unroll
       for (int m = 0; m < MR; ++m) {
-        const float v = lane_group_sum<32>(fmaf(s, P[m], cb * sx[m]));
+        const float Pm = BITS == 2 ? P[m] - ox[m] : P[m];
+        const float v = lane_group_sum<32>(fmaf(s, Pm, cb * sx[m]));
         if (li == 31) part[par][(wave * RW + 2 * i + r) * MR + m] = v;
       }
     }
@@ -257,7 +295,7 @@ int resident_blocks(int nw) {
   int v = cache[nw].load(std::memory_order_relaxed);
   if (v > 0) return v;
   int per_cu = 0, dev = 0, cus = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, qmv_split_kernel<BITS, MR, S, max_waves(MR)>,
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, qmv_split_kernel<BITS, MR, S, max_waves(MR, BITS)>,
                                                    64 * nw, 0) != hipSuccess || per_cu < 1)
     per_cu = 1;
   if (hipGetDevice(&dev) != hipSuccess ||
@@ -275,7 +313,7 @@ hipError_t launch_s(const Params& p, hipStream_t stream) {
   const int nblk = (p.N + 2 * S - 1) / (2 * S);
   const unsigned rows = gemv_grid_rows(p.bt);
   const int grid = std::max(1, std::min(nblk, resident_blocks<BITS, MR, S>(nw) / (int)rows));
-  hipLaunchKernelGGL((qmv_split_kernel<BITS, MR, S, max_waves(MR)>), dim3(grid, rows), dim3(64 * nw), 0,
+  hipLaunchKernelGGL((qmv_split_kernel<BITS, MR, S, max_waves(MR, BITS)>), dim3(grid, rows), dim3(64 * nw), 0,
                      stream, p);
   return hipGetLastError();
 }
@@ -288,20 +326,25 @@ hipError_t launch_mr(const Params& p, hipStream_t stream) {
 // Caller guarantees fits(K, BITS, mr).
 template <int BITS>
 hipError_t launch_bits(const Params& p, int mr, hipStream_t stream) {
-  switch (mr) {
-    case 1: return launch_mr<BITS, 1>(p, stream);
-    case 2: return launch_mr<BITS, 2>(p, stream);
-    case 3: return launch_mr<BITS, 3>(p, stream);
-    case 4: return launch_mr<BITS, 4>(p, stream);
-    case 5: return launch_mr<BITS, 5>(p, stream);
-    case 6: return launch_mr<BITS, 6>(p, stream);
-    case 7: return launch_mr<BITS, 7>(p, stream);
-    default: return launch_mr<BITS, 8>(p, stream);
+  if constexpr (BITS == 2) {
+    return mr == 1 ? launch_mr<2, 1>(p, stream) : mr == 2 ? launch_mr<2, 2>(p, stream) : launch_mr<2, 3>(p, stream);
+  } else {
+    switch (mr) {
+      case 1: return launch_mr<BITS, 1>(p, stream);
+      case 2: return launch_mr<BITS, 2>(p, stream);
+      case 3: return launch_mr<BITS, 3>(p, stream);
+      case 4: return launch_mr<BITS, 4>(p, stream);
+      case 5: return launch_mr<BITS, 5>(p, stream);
+      case 6: return launch_mr<BITS, 6>(p, stream);
+      case 7: return launch_mr<BITS, 7>(p, stream);
+      default: return launch_mr<BITS, 8>(p, stream);
+    }
   }
 }
 
 }  // namespace qmv_split_detail
 
+extern template hipError_t qmv_split_detail::launch_bits<2>(const qmv_split_detail::Params&, int, hipStream_t);
 extern template hipError_t qmv_split_detail::launch_bits<4>(const qmv_split_detail::Params&, int, hipStream_t);
 extern template hipError_t qmv_split_detail::launch_bits<8>(const qmv_split_detail::Params&, int, hipStream_t);
 

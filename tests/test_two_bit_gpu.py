@@ -1,7 +1,8 @@
 """GPU parity for 2-bit codes (16 per word, LSB first; groups of 64 and 128) on every
-entry point: the GEMV paths (qmv, qmm with M < 8, gather_qmv; the general kernel, codes
-spread to nibbles) are held to the f32 rule, the matrix-core paths (qmm with M >= 8,
-both grouped GEMMs) to the bf16 rule; integer-valued inputs must match exactly."""
+entry point: the GEMV paths (qmv, qmm with M < 8, gather_qmv; the split-K kernel up to
+3 rows, the general kernel with codes spread to nibbles beyond) are held to the f32
+rule, the matrix-core paths (qmm with M >= 8, both grouped GEMMs) to the bf16 rule;
+integer-valued inputs must match exactly."""
 
 import numpy as np
 import pytest
@@ -24,7 +25,8 @@ def _gpu():
     t.cuda.synchronize()
 
 
-SHAPES = [(1, 300, 1024), (1, 70, 5120), (3, 133, 2048), (5, 40, 4096), (7, 33, 384), (1, 9, 20480),
+SHAPES = [(1, 300, 1024), (1, 70, 5120), (3, 133, 2048), (2, 61, 16384), (3, 45, 5120), (5, 40, 4096),
+          (7, 33, 384), (1, 9, 20480),
           (8, 70, 256), (40, 129, 1024), (300, 200, 2048), (96, 64, 2560), (70, 66, 5120)]
 
 
@@ -44,7 +46,8 @@ def test_two_bit_dense(M, N, K, group):
         G.assert_close(got, want, "f32", f"2-bit qmv g{group} M{M} N{N} K{K}")
 
 
-@pytest.mark.parametrize("fn,M", [("bitmm_qmv", 1), ("bitmm_qmm", 5), ("bitmm_qmm", 130)])
+@pytest.mark.parametrize("fn,M", [("bitmm_qmv", 1), ("bitmm_qmm", 2), ("bitmm_qmm", 3), ("bitmm_qmm", 5),
+                                  ("bitmm_qmm", 130)])
 def test_two_bit_integer_exact(fn, M):
     rng = np.random.default_rng(M)
     N, K = 97, 2048
