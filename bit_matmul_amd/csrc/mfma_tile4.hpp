@@ -213,13 +213,17 @@ struct MmTile4 {
         r.b = __builtin_amdgcn_raw_buffer_load_b16(rb, soff, gidx_uniform(gc) * 2, 0);
       }
     };
-    // WS, 4 bits: groups ge, ge+1 (ge even) of rows 0-15 and 16-31. The 64-byte span may
-    // pass the row end when ge = G-1; its offset is in the checked per-lane part, so
-    // past the last row of W it reads zeros.
+    // WS, 4 bits: groups ge, ge+1 (ge even) of rows 0-15 and 16-31 (one 64-byte span per
+    // row). Rows past N read zeros through the checked per-lane offset.
     auto load_pair = [&](int ge, Wraw& r0, Wraw& r1) {
-      const uint32_t go = (uint32_t)(min(ge, (G - 1) & ~1) * GB);
-      r0.q[0] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rw, wsx + go, 0, 0));
-      r1.q[0] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rw, wsy + go, 0, 0));
+      const int gp = min(ge, (G - 1) & ~1);
+      const uint32_t go = (uint32_t)(gp * GB);
+      // With G odd the last pair has one group: the lanes of the missing second group
+      // read nothing (an offset past every descriptor) instead of the next row's first
+      // bytes, which would cost a second fetch of that line.
+      const uint32_t past = (gp + 1 < G || wchunk < 2) ? 0u : 0x80000000u;
+      r0.q[0] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rw, (wsx + go) | past, 0, 0));
+      r1.q[0] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rw, (wsy + go) | past, 0, 0));
       if constexpr (SBM == 0) {
         r0.s = __builtin_amdgcn_raw_buffer_load_b16(rs, soff, gidx_uniform(min(ge, G - 1)) * 2, 0);
         r0.b = __builtin_amdgcn_raw_buffer_load_b16(rb, soff, gidx_uniform(min(ge, G - 1)) * 2, 0);
