@@ -1,7 +1,9 @@
 """Build libbitmm.so for gfx950 with hipcc, in-tree.
 
 Every translation unit under ``csrc/`` is compiled in parallel into ``_build/`` and
-linked into ``bit_matmul_amd/libbitmm.so``. Run ``python -m bit_matmul_amd.build``.
+linked into ``bit_matmul_amd/libbitmm.so``. The benchmark's measurement kernels
+(``probe/probe.hip``: a streaming read and a matrix-core loop, not part of the library)
+are linked into ``bit_matmul_amd/libbitmm_probe.so``. Run ``python -m bit_matmul_amd.build``.
 """
 
 from __future__ import annotations
@@ -17,6 +19,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libbitmm.so")
+PROBE_SRC = os.path.join(HERE, "probe", "probe.hip")
+PROBE_LIB = os.path.join(HERE, "libbitmm_probe.so")
 ARCH = "gfx950"
 
 # Packed-FP32 VALU instructions are kept out of the device code.
@@ -47,20 +51,27 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(jobs: int | None = None, verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    srcs = sources()
-    jobs = jobs or min(len(srcs), max(1, (os.cpu_count() or 4)))
-    with cf.ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB + f".tmp{os.getpid()}"
+def _link(objs, out: str) -> None:
+    tmp = out + f".tmp{os.getpid()}"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+
+
+def build(jobs: int | None = None, verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = sources()
+    jobs = jobs or min(len(srcs) + 1, max(1, (os.cpu_count() or 4)))
+    with cf.ThreadPoolExecutor(jobs) as ex:
+        probe_obj = ex.submit(_compile, PROBE_SRC)
+        objs = list(ex.map(_compile, srcs))
+        probe_obj = probe_obj.result()
+    _link(objs, LIB)
+    _link([probe_obj], PROBE_LIB)
     if verbose:
-        print(f"built {LIB} from {len(srcs)} sources", file=sys.stderr)
+        print(f"built {LIB} from {len(srcs)} sources, and {PROBE_LIB}", file=sys.stderr)
     return LIB
 
 
