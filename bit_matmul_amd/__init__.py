@@ -48,7 +48,7 @@ GROUP = 64
 
 __all__ = [
     "BitmmError", "lib", "bitmm_abi_version", "bitmm_status_string", "bitmm_qmv", "bitmm_qmm",
-    "bitmm_gather_qmm_workspace_bytes", "bitmm_gather_qmm", "bitmm_gather_qmv",
+    "bitmm_gather_qmm_workspace_bytes", "bitmm_gather_qmm", "bitmm_gather_qmm_noalloc", "bitmm_gather_qmv",
     "bitmm_gather_qmm_indexed_workspace_bytes", "bitmm_gather_qmm_indexed", "qmv", "qmm",
     "gather_qmm", "gather_qmv", "gather_qmm_indexed", "bitmm_gather_mm_workspace_bytes",
     "bitmm_gather_mm", "gather_mm",
@@ -91,6 +91,8 @@ def lib() -> ctypes.CDLL:
         L.bitmm_gather_qmm_workspace_bytes.restype = SZ
         L.bitmm_gather_qmm.argtypes = [P, P, P, P, P, P, I64, I64, I64, I64, I, I, I, P, SZ, P]
         L.bitmm_gather_qmm.restype = I
+        L.bitmm_gather_qmm_noalloc.argtypes = [P, P, P, P, P, P, I64, I64, I64, I64, I, I, I, P, P]
+        L.bitmm_gather_qmm_noalloc.restype = I
         L.bitmm_gather_qmv.argtypes = [P, P, P, P, P, P, P, I64, I64, I64, I64, I64, I, I, I, P]
         L.bitmm_gather_qmv.restype = I
         L.bitmm_gather_qmm_indexed_workspace_bytes.argtypes = [I64, I64, I64]
@@ -231,6 +233,33 @@ def bitmm_gather_qmm(x, w, scales, biases, expert_idx, y, workspace, bits: int,
                                 _ptr(workspace), workspace.numel(), _stream_ptr(stream, dev))
     if st != BITMM_OK:
         raise BitmmError(st, "bitmm_gather_qmm")
+    return y
+
+
+def bitmm_gather_qmm_noalloc(x, w, scales, biases, expert_idx, y, bits: int, group_size: int = GROUP,
+                             status=None, stream=None):
+    """bitmm_gather_qmm without a workspace: the library's static per-GPU workspace is
+    used and nothing is allocated. `status` (optional int32 tensor of one element on the
+    device) receives the precondition status word (0, or 1 + the first offending row)."""
+    torch = _torch()
+    B, K = x.shape
+    E, N = w.shape[0], w.shape[1]
+    dev = x.device
+    _expect(x, "x", torch.bfloat16, (B, K), dev)
+    if K % group_size:
+        raise ValueError(f"K={K} is not a multiple of group_size={group_size}")
+    _expect(w, "w", torch.int32, (E, N, K * bits // 32), dev)
+    _expect(scales, "scales", torch.bfloat16, (E, N, K // group_size), dev)
+    _expect(biases, "biases", torch.bfloat16, (E, N, K // group_size), dev)
+    _expect(expert_idx, "expert_idx", torch.int32, (B,), dev)
+    _expect(y, "y", y.dtype, (B, N), dev)
+    if status is not None:
+        _expect(status, "status", torch.int32, (1,), dev)
+    st = lib().bitmm_gather_qmm_noalloc(_ptr(x), _ptr(w), _ptr(scales), _ptr(biases), _ptr(expert_idx),
+                                        _ptr(y), B, N, K, E, int(bits), int(group_size), _out_code(y),
+                                        None if status is None else _ptr(status), _stream_ptr(stream, dev))
+    if st != BITMM_OK:
+        raise BitmmError(st, "bitmm_gather_qmm_noalloc")
     return y
 
 

@@ -167,6 +167,37 @@ bitmm_status bitmm_gather_qmm(const void* x, const uint32_t* w, const void* scal
   }
 }
 
+bitmm_status bitmm_gather_qmm_noalloc(const void* x, const uint32_t* w, const void* scales,
+                                      const void* biases, const int32_t* expert_idx, void* y,
+                                      int64_t B, int64_t N, int64_t K, int64_t E, int bits,
+                                      int group_size, bitmm_out out, uint32_t* status,
+                                      void* stream) {
+  try {
+    if (!group_ok(group_size) || !bits_ok(bits, group_size)) return BITMM_ERR_UNSUPPORTED;
+    if (out != BITMM_OUT_BF16 && out != BITMM_OUT_F32) return BITMM_ERR_UNSUPPORTED;
+    if (B < 0 || N < 0 || K < 1 || E < 1 || K % group_size != 0 || K % 64 != 0) return BITMM_ERR_SHAPE;
+    if (B > INT32_MAX || N > INT32_MAX || K > INT32_MAX || E > INT32_MAX - 2)
+      return BITMM_ERR_SHAPE;
+    // The static workspace holds the status word and E + 1 offsets.
+    if (E > bitmm::gather_noalloc_max_experts()) return BITMM_ERR_UNSUPPORTED;
+    if (B == 0 || N == 0) return BITMM_OK;
+    if (!x || !w || !scales || !biases || !expert_idx || !y) return BITMM_ERR_NULL;
+    if (!aligned(x, 16) || !aligned(w, 16) || !aligned(scales, 2) || !aligned(biases, 2) ||
+        !aligned(expert_idx, 4) || !aligned(status, 4) || !aligned(y, out == BITMM_OUT_F32 ? 4 : 2))
+      return BITMM_ERR_ALIGN;
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    bitmm_status st = device_check(hs);
+    if (st != BITMM_OK) return st;
+    hipError_t e = bitmm::launch_gather_qmm_noalloc(
+        static_cast<const uint16_t*>(x), w, static_cast<const uint16_t*>(scales),
+        static_cast<const uint16_t*>(biases), expert_idx, y, B, N, K, E, bits, group_size,
+        out == BITMM_OUT_F32, status, hs);
+    return e == hipSuccess ? BITMM_OK : BITMM_ERR_LAUNCH;
+  } catch (...) {
+    return BITMM_ERR_LAUNCH;
+  }
+}
+
 size_t bitmm_gather_qmm_indexed_workspace_bytes(int64_t B, int64_t N, int64_t E) {
   if (B < 0 || N < 0 || E < 1 || E > INT32_MAX - 2 || B > INT32_MAX) return 0;
   return bitmm::gather_indexed_workspace_bytes(B, E);

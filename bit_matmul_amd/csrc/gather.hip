@@ -12,6 +12,9 @@
 //      row range from the workspace and runs the shared matrix-core tile over those
 //      rows, so each expert's codes are streamed once per column block however many
 //      rows the expert has. Experts without rows exit at once.
+#include <atomic>
+#include <mutex>
+
 #include "kernels.hpp"
 #include "mfma_tile4.hpp"
 
@@ -26,10 +29,12 @@ constexpr int kPrepThreads = 1024;
 // from a (the previous row's id, -1 before row 0) to c, the offsets of the experts
 // a+1 .. c are that row; past the last row, the offsets of the experts after its id
 // are B. With valid ids each offset is written exactly once; with invalid ones the
-// offsets are not meaningful and the grouped GEMM does not read them.
+// offsets are not meaningful and the grouped GEMM does not read them. The status word
+// is also written to `status` when that is not null.
 __global__ __launch_bounds__(kPrepThreads) void gather_prepare_kernel(const int32_t* __restrict__ idx,
                                                                       int B, int E,
-                                                                      uint32_t* __restrict__ ws) {
+                                                                      uint32_t* __restrict__ ws,
+                                                                      uint32_t* __restrict__ status) {
   __shared__ int first_bad;
   if (threadIdx.x == 0) first_bad = B;
   __syncthreads();
@@ -52,7 +57,11 @@ __global__ __launch_bounds__(kPrepThreads) void gather_prepare_kernel(const int3
     for (int e = threadIdx.x; e <= E; e += kPrepThreads) off[e] = 0;
   if (mine < B) atomicMin(&first_bad, mine);
   __syncthreads();
-  if (threadIdx.x == 0) ws[0] = first_bad < B ? (uint32_t)first_bad + 1u : 0u;
+  if (threadIdx.x == 0) {
+    const uint32_t v = first_bad < B ? (uint32_t)first_bad + 1u : 0u;
+    ws[0] = v;
+    if (status) *status = v;
+  }
 }
 
 // Indexed form: rows in any order, an optional token index. One workgroup builds a
@@ -290,13 +299,63 @@ size_t gather_workspace_bytes(int64_t E) {
   return (raw + 255) / 256 * 256;
 }
 
+namespace {
+
+// Workspace of the allocation-free entry point (status word and per-expert offsets),
+// one copy per GPU for the life of the process. Every call on a GPU uses that GPU's
+// copy, so calls that overlap on one GPU race on it.
+constexpr size_t kScratchBytes = 64 * 1024;
+static __device__ __align__(256) uint32_t scratch[kScratchBytes / sizeof(uint32_t)];
+
+constexpr int kMaxScratchDevices = 64;
+std::atomic<void*> g_scratch[kMaxScratchDevices];
+std::mutex g_scratch_mu;
+
+// Device address of the current GPU's `scratch`, looked up once per device with that
+// device current (the host-side name of the array is not a device address).
+hipError_t scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess || p == nullptr) return e != hipSuccess ? e : hipErrorInvalidSymbol;
+      g_scratch[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return hipSuccess;
+}
+
+}  // namespace
+
+int64_t gather_noalloc_max_experts() {
+  return (int64_t)(kScratchBytes / sizeof(uint32_t)) - 2;  // (E + 2) words fit
+}
+
+hipError_t launch_gather_qmm_noalloc(const uint16_t* x, const uint32_t* w, const uint16_t* scales,
+                                     const uint16_t* biases, const int32_t* expert_idx, void* y,
+                                     int64_t B, int64_t N, int64_t K, int64_t E, int bits, int group,
+                                     bool out_f32, uint32_t* status, hipStream_t stream) {
+  void* ws = nullptr;
+  const hipError_t e = scratch_address(&ws);
+  if (e != hipSuccess) return e;
+  return launch_gather_qmm(x, w, scales, biases, expert_idx, y, B, N, K, E, bits, group, out_f32, ws,
+                           stream, status);
+}
+
 hipError_t launch_gather_qmm(const uint16_t* x, const uint32_t* w, const uint16_t* scales,
                              const uint16_t* biases, const int32_t* expert_idx, void* y,
                              int64_t B, int64_t N, int64_t K, int64_t E, int bits, int group,
-                             bool out_f32, void* workspace, hipStream_t stream) {
+                             bool out_f32, void* workspace, hipStream_t stream, uint32_t* status) {
   uint32_t* ws = static_cast<uint32_t*>(workspace);
   hipLaunchKernelGGL(gather_prepare_kernel, dim3(1), dim3(kPrepThreads), 0, stream, expert_idx,
-                     (int)B, (int)E, ws);
+                     (int)B, (int)E, ws, status);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   GatherParams p;

@@ -31,12 +31,21 @@ hipError_t launch_qmm_mfma(const uint16_t* x, const uint32_t* w, const uint16_t*
                            int bits, int group, bool out_f32, hipStream_t stream);
 
 // Expert-gathered GEMM: prepare (validation + per-expert offsets into workspace),
-// then the grouped matrix-core kernel.
+// then the grouped matrix-core kernel. The status word also goes to `status` if not null.
 size_t gather_workspace_bytes(int64_t E);
 hipError_t launch_gather_qmm(const uint16_t* x, const uint32_t* w, const uint16_t* scales,
                              const uint16_t* biases, const int32_t* expert_idx, void* y,
                              int64_t B, int64_t N, int64_t K, int64_t E, int bits, int group,
-                             bool out_f32, void* workspace, hipStream_t stream);
+                             bool out_f32, void* workspace, hipStream_t stream,
+                             uint32_t* status = nullptr);
+
+// The same with the library's per-GPU static workspace (no allocation, no workspace
+// argument); E at most gather_noalloc_max_experts().
+int64_t gather_noalloc_max_experts();
+hipError_t launch_gather_qmm_noalloc(const uint16_t* x, const uint32_t* w, const uint16_t* scales,
+                                     const uint16_t* biases, const int32_t* expert_idx, void* y,
+                                     int64_t B, int64_t N, int64_t K, int64_t E, int bits, int group,
+                                     bool out_f32, uint32_t* status, hipStream_t stream);
 
 // Indexed GatherQMM (rows in any order, optional token index): a counting sort of the
 // rows by expert into the workspace, then the grouped GEMM over the sorted rows.

@@ -41,7 +41,9 @@
  *
  * Conventions.
  *   - Pointers are DEVICE pointers owned by the caller; nothing is retained after
- *     the call returns and the library allocates no memory.
+ *     the call returns and the library allocates no memory (the one exception,
+ *     bitmm_gather_qmm_noalloc, uses a fixed 64 KiB array that the library holds per
+ *     GPU from load time on).
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream) and the
  *     call returns without synchronising. Calls are re-entrant and may run
  *     concurrently on different streams. Results are bitwise deterministic.
@@ -146,6 +148,27 @@ bitmm_status bitmm_gather_qmm(const void* x, const uint32_t* w, const void* scal
                               int64_t N, int64_t K, int64_t E, int bits, int group_size,
                               bitmm_out out, void* workspace, size_t workspace_bytes,
                               void* stream);
+
+/*
+ * bitmm_gather_qmm without a workspace argument and without any allocation, for callers
+ * that cannot allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation. Same operation, arguments, precondition check and
+ * results as bitmm_gather_qmm; the status word and the expert offsets go to a workspace
+ * of 64 KiB that the library keeps in device memory, one per GPU, for the life of the
+ * process (it holds whatever the last call left there; every word a call reads was
+ * written earlier by the same call).
+ *   status: optional device pointer (uint32, 4-byte aligned; NULL = not reported) that
+ *           receives the status word: 0 if the precondition holds, otherwise 1 + the
+ *           first offending row (y is then all zeros).
+ * Limit: E <= 16382 (else BITMM_ERR_UNSUPPORTED). Every call on one GPU uses that GPU's
+ * workspace, so calls that may overlap on one GPU (different streams without ordering)
+ * race; order them on one stream, or use bitmm_gather_qmm with workspaces of their own.
+ */
+bitmm_status bitmm_gather_qmm_noalloc(const void* x, const uint32_t* w, const void* scales,
+                                      const void* biases, const int32_t* expert_idx, void* y,
+                                      int64_t B, int64_t N, int64_t K, int64_t E, int bits,
+                                      int group_size, bitmm_out out, uint32_t* status,
+                                      void* stream);
 
 /*
  * Bytes of device workspace bitmm_gather_qmm_indexed needs for B rows, N columns and E

@@ -45,7 +45,7 @@ def test_exports_every_declared_function(L):
     names = header_functions()
     assert set(names) == {"bitmm_abi_version", "bitmm_status_string", "bitmm_qmv", "bitmm_qmm",
                           "bitmm_gather_qmm_workspace_bytes", "bitmm_gather_qmm",
-                          "bitmm_gather_qmv", "bitmm_gather_qmm_indexed_workspace_bytes",
+                          "bitmm_gather_qmm_noalloc", "bitmm_gather_qmv", "bitmm_gather_qmm_indexed_workspace_bytes",
                           "bitmm_gather_qmm_indexed", "bitmm_gather_mm_workspace_bytes",
                           "bitmm_gather_mm"}
     for n in names:
@@ -181,6 +181,47 @@ def test_gather_validation(L, kw, expected):
             pytest.skip("fake pointers would reach a real device")
         expected = bm.BITMM_ERR_DEVICE
     assert L.bitmm_gather_qmm(*gather_args(**kw)) == expected
+
+
+def noalloc_args(**kw):
+    a = dict(x=A, w=A + 0x1000, s=A + 0x2000, b=A + 0x3000, idx=A + 0x4000, y=A + 0x5000,
+             B=4584, N=704, K=2816, E=128, bits=4, group=64, out=0, status=A + 0x6000, stream=0)
+    a.update(kw)
+    return [ctypes.c_void_p(a["x"]), ctypes.c_void_p(a["w"]), ctypes.c_void_p(a["s"]),
+            ctypes.c_void_p(a["b"]), ctypes.c_void_p(a["idx"]), ctypes.c_void_p(a["y"]), a["B"],
+            a["N"], a["K"], a["E"], a["bits"], a["group"], a["out"], ctypes.c_void_p(a["status"]),
+            ctypes.c_void_p(a["stream"])]
+
+
+NOALLOC_CASES = [
+    (dict(bits=5), bm.BITMM_ERR_UNSUPPORTED),
+    (dict(group=16), bm.BITMM_ERR_UNSUPPORTED),
+    (dict(out=2), bm.BITMM_ERR_UNSUPPORTED),
+    (dict(E=16383), bm.BITMM_ERR_UNSUPPORTED),  # beyond the static workspace
+    (dict(E=16383, B=0), bm.BITMM_ERR_UNSUPPORTED),
+    (dict(E=0), bm.BITMM_ERR_SHAPE),
+    (dict(K=700), bm.BITMM_ERR_SHAPE),
+    (dict(B=-1), bm.BITMM_ERR_SHAPE),
+    (dict(B=0), bm.BITMM_OK),
+    (dict(N=0), bm.BITMM_OK),
+    (dict(idx=0), bm.BITMM_ERR_NULL),
+    (dict(y=0), bm.BITMM_ERR_NULL),
+    (dict(idx=A + 2), bm.BITMM_ERR_ALIGN),
+    (dict(status=A + 2), bm.BITMM_ERR_ALIGN),
+    (dict(x=A + 2), bm.BITMM_ERR_ALIGN),
+    (dict(), None),
+    (dict(status=0), None),    # the status word is optional
+    (dict(E=16382), None),     # the largest expert count the static workspace holds
+]
+
+
+@pytest.mark.parametrize("kw,expected", NOALLOC_CASES)
+def test_gather_noalloc_validation(L, kw, expected):
+    if expected is None:
+        if gpu_present():
+            pytest.skip("fake pointers would reach a real device")
+        expected = bm.BITMM_ERR_DEVICE
+    assert L.bitmm_gather_qmm_noalloc(*noalloc_args(**kw)) == expected
 
 
 def gqmv_args(**kw):
