@@ -72,6 +72,7 @@ HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix, published
 ROTATE_BYTES = 1 << 30
 CU_NUM, SIMD_NUM = 256, 1024    # MI355X compute units and SIMDs (counter normalisation)
+XCD_NUM = 8                     # GRBM_GUI_ACTIVE comes summed over the 8 XCDs' counters
 
 HEADLINE = ("qmv_M1_K5120_N5120_b4", "qmv_M1_K5120_N13824_b4")
 TRACE_SUMMARY = "hot_path_kernel_trace"
@@ -557,14 +558,17 @@ def _pct(v, q):
 
 
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
-CALIB_BYTES = 256 << 20   # --calibrate-copy: five device copies of this size
+CALIB_BYTES = 256 << 20   # --calibrate-copy: the first CALIB_COPIES device copies of the run
+CALIB_COPIES = 5
 
 
 def summarize_counters(files, algorithmic_bytes=None):
     """Counter values per dispatch, averaged over the dispatches of each kernel of the
-    library; derived utilisations; HBM traffic per call from FETCH_SIZE and WRITE_SIZE,
-    each scaled by what the counter reads for the calibration copies of CALIB_BYTES
-    (the device copies with the largest grid in the run)."""
+    library; derived utilisations (GRBM_GUI_ACTIVE, reported as the sum over the XCDs,
+    divided by XCD_NUM is the kernel's cycle count); HBM traffic per call from FETCH_SIZE
+    and WRITE_SIZE, each scaled by what the counter reads for the calibration copies of
+    CALIB_BYTES (the first CALIB_COPIES device copies of each run: bench.py makes them
+    before anything else)."""
     out = []
     vals = {}
     copies = {}
@@ -578,8 +582,8 @@ def summarize_counters(files, algorithmic_bytes=None):
             if name is None or cn is None or cv is None:
                 continue
             if COPY_KERNEL in name:
-                copies.setdefault(int(grid or 0), {}).setdefault(cn, {}).setdefault((fi, did), 0.0)
-                copies[int(grid or 0)][cn][(fi, did)] += float(cv)
+                copies.setdefault(cn, {}).setdefault(fi, {}).setdefault(int(did or 0), 0.0)
+                copies[cn][fi][int(did or 0)] += float(cv)
                 continue
             if "bitmm" not in name:
                 continue
@@ -588,15 +592,20 @@ def summarize_counters(files, algorithmic_bytes=None):
             vals[key][cn][(fi, did)] += float(cv)
     scale = {}
     if copies:
-        big = copies[max(copies)]
-        out.append(f"# calibration: the device copies of {CALIB_BYTES >> 10} KiB (largest copy grid in the run)")
-        for cn, want in (("FETCH_SIZE", CALIB_BYTES / 1024), ("WRITE_SIZE", CALIB_BYTES / 1024)):
-            if cn in big:
-                raw = float(np.mean(list(big[cn].values())))
-                out.append(f"copy_{cn.lower()}_kib: {raw:.1f}")
-                if raw > 0:
-                    scale[cn] = want / raw
-                    out.append(f"{cn.lower().replace('_size', '')}_scale: {scale[cn]:.5f}")
+        out.append(f"# calibration: the first {CALIB_COPIES} device copies of each run ({CALIB_BYTES >> 10} KiB each)")
+        for cn in ("FETCH_SIZE", "WRITE_SIZE"):
+            if cn not in copies:
+                continue
+            first = []
+            for fi, byd in copies[cn].items():
+                first += [byd[d] for d in sorted(byd)[:CALIB_COPIES]]
+            raw = float(np.mean(first))
+            spread = (max(first) - min(first)) / raw if raw > 0 else float("inf")
+            out.append(f"copy_{cn.lower()}_kib: {raw:.1f}")
+            out.append(f"# spread over the calibration copies: {100 * spread:.2f} %")
+            if raw > 0 and spread < 0.05:
+                scale[cn] = CALIB_BYTES / 1024 / raw
+                out.append(f"{cn.lower().replace('_size', '')}_scale: {scale[cn]:.5f}")
     out.append("# counters per dispatch, averaged over the dispatches of each kernel (grid in work-items)")
     main, main_g = None, -1.0
     traffic = 0.0
@@ -608,6 +617,7 @@ def summarize_counters(files, algorithmic_bytes=None):
         for cn, v in sorted(avg.items()):
             out.append(f"#   {cn}: {v:.1f}")
         g = avg.get("GRBM_GUI_ACTIVE")
+        g = g / XCD_NUM if g else g
         derived = {}
         if g:
             if "SQ_VALU_MFMA_BUSY_CYCLES" in avg:
@@ -760,6 +770,16 @@ def main():
     only = [s for s in args.only.split(",") if s] if args.only else None
 
     result = {}
+    if args.calibrate_copy:
+        # first of all, so that these are the run's first device copies
+        src = torch.ones(CALIB_BYTES, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(CALIB_COPIES):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        result["calibration_copy_bytes"] = CALIB_BYTES
+        del src, dst
+        torch.cuda.empty_cache()
     ceilings = None
     pa = pb = None
     gpu_time = {}
@@ -773,7 +793,7 @@ def main():
         log(f"inputs generated in {time.perf_counter() - t0:.1f} s")
         ca = Case(torch, pa, "qmv", torch.bfloat16)
         cb = Case(torch, pb, "qmv", torch.bfloat16)
-        reps = time_steps(torch, [ca, cb], args.steps, args.warmup, R, markers, "headline_step")
+        reps = time_steps(torch, [ca, cb], args.steps, args.warmup, R)
         total, spread = stats(reps, 1)
         total /= 1e6
         step_bytes = ca.bytes + cb.bytes
@@ -820,17 +840,6 @@ def main():
         for e in result["per_kernel"]:
             attach_profiles(e, src_hash)
         del ca, cb
-        torch.cuda.empty_cache()
-
-    if args.calibrate_copy:
-        n = 256 << 20
-        src = torch.ones(n, dtype=torch.uint8, device="cuda")
-        dst = torch.empty_like(src)
-        for _ in range(5):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        result["calibration_copy_bytes"] = n
-        del src, dst
         torch.cuda.empty_cache()
 
     # ---- the rest of the hot path ------------------------------------------

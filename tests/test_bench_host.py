@@ -57,19 +57,19 @@ CC = ["Correlation_Id", "Dispatch_Id", "Agent_Id", "Queue_Id", "Process_Id", "Th
 def test_counter_summary_calibration_and_derived(tmp_path):
     copy = bench.COPY_KERNEL + "(void*)"
     fetch_rows, write_rows, sq_rows = [], [], []
-    for d in range(5):   # calibration copies of 256 MiB: FETCH reads half, WRITE all
-        fetch_rows.append([d, d, 1, 1, 1, 1, 67108864, 7, copy, 256, "FETCH_SIZE", 131072.0])
-        write_rows.append([d, d, 1, 1, 1, 1, 67108864, 7, copy, 256, "WRITE_SIZE", 262144.0])
-    fetch_rows.append([5, 5, 1, 1, 1, 1, 1024, 8, copy, 256, "FETCH_SIZE", 3.0])  # a small copy
+    for d in range(5):   # calibration copies of 256 MiB, first in the run: FETCH reads half, WRITE all
+        fetch_rows.append([d, d, 1, 1, 1, 1, 131072, 7, copy, 256, "FETCH_SIZE", 131072.0])
+        write_rows.append([d, d, 1, 1, 1, 1, 131072, 7, copy, 256, "WRITE_SIZE", 262144.0])
+    fetch_rows.append([5, 5, 1, 1, 1, 1, 131072, 7, copy, 256, "FETCH_SIZE", 3.0])  # a later, smaller copy
     for d in range(10, 14):
         fetch_rows.append([d, d, 1, 1, 1, 1, 3072, 2, GEMM, 256, "FETCH_SIZE", 1000.0])
         fetch_rows.append([d + 10, d + 10, 1, 1, 1, 1, 1024, 3, PREP, 1024, "FETCH_SIZE", 10.0])
         write_rows.append([d, d, 1, 1, 1, 1, 3072, 2, GEMM, 256, "WRITE_SIZE", 300.0])
         write_rows.append([d + 10, d + 10, 1, 1, 1, 1, 1024, 3, PREP, 1024, "WRITE_SIZE", 1.0])
         sq_rows.append([d, d, 1, 1, 1, 1, 3072, 2, GEMM, 256, "SQ_VALU_MFMA_BUSY_CYCLES", 512000.0])
-        sq_rows.append([d, d, 1, 1, 1, 1, 3072, 2, GEMM, 256, "GRBM_GUI_ACTIVE", 2000.0])
+        sq_rows.append([d, d, 1, 1, 1, 1, 3072, 2, GEMM, 256, "GRBM_GUI_ACTIVE", 2000.0 * bench.XCD_NUM])
         sq_rows.append([d, d, 1, 1, 1, 1, 3072, 2, GEMM, 256, "SQ_ACTIVE_INST_VALU", 256000.0])
-        sq_rows.append([d + 10, d + 10, 1, 1, 1, 1, 1024, 3, PREP, 1024, "GRBM_GUI_ACTIVE", 100.0])
+        sq_rows.append([d + 10, d + 10, 1, 1, 1, 1, 1024, 3, PREP, 1024, "GRBM_GUI_ACTIVE", 100.0 * bench.XCD_NUM])
     # the passes come from separate runs whose dispatch ids collide
     _write(str(tmp_path / "fetch" / "h" / "1_counter_collection.csv"), CC, fetch_rows)
     _write(str(tmp_path / "write" / "h" / "2_counter_collection.csv"), CC, write_rows)
