@@ -4,8 +4,11 @@
 //   qmv_split_kernel (qmv_split.hpp): up to 8 activation rows with K split across the
 //     waves of a workgroup (K <= 16384 at 4 bits and 8192 at 8 bits for up to 3 rows,
 //     half that from 4 rows; 2 bits: up to 3 rows, K <= 16384), the small-M prefill tail;
+//   qmv_mfma_kernel (qmv_mfma.hpp): 2 to 8 activation rows on the matrix cores (K <= 16384
+//     at 4 bits, 8192 at 8, 32768 at 2; more rows in launches of 8), the small-M prefill
+//     tail;
 //   qmv_kernel (qmv_impl.hpp): up to 8 activation rows per launch, any K (several
-//     passes over K when a row does not fit), for what the other two do not take (2-bit
+//     passes over K when a row does not fit), for what the others do not take (2-bit
 //     codes with K past the split kernel's range: four rows per launch).
 #include <stdlib.h>
 
@@ -14,6 +17,7 @@
 #include "kernels.hpp"
 #include "qmv_dma.hpp"
 #include "qmv_impl.hpp"
+#include "qmv_mfma.hpp"
 #include "qmv_split.hpp"
 
 namespace bitmm {
@@ -80,6 +84,29 @@ hipError_t launch_rows(const uint16_t* x, const uint32_t* w, const uint16_t* sca
     return bits == 4   ? qmv_dma_detail::launch_bits<4>(dp, compute_units(), wpc, stream)
            : bits == 2 ? qmv_dma_detail::launch_bits<2>(dp, compute_units(), wpc, stream)
                        : qmv_dma_detail::launch_bits<8>(dp, compute_units(), wpc, stream);
+  }
+  // Dense calls with several rows: the matrix-core GEMV, eight rows per launch.
+  if (forced_path() == 0 && bt.exp == nullptr && M >= 2 && qmv_mfma_detail::fits(K, bits, M < 8 ? M : 8)) {
+    for (int64_t m0 = 0; m0 < M; m0 += 8) {
+      qmv_mfma_detail::Params mp;
+      mp.x = x + m0 * K;
+      mp.w = w;
+      mp.s = scales;
+      mp.b = biases;
+      mp.y = static_cast<char*>(y) + (size_t)(m0 * N) * ysz;
+      mp.M = (int)(M - m0 < 8 ? M - m0 : 8);
+      mp.N = (int)N;
+      mp.K = (int)K;
+      mp.gshift = group_shift(group);
+      mp.out_f32 = out_f32 ? 1 : 0;
+      mp.mask = 0x000F000Fu;
+      mp.magic = 0x43004300u;
+      const hipError_t e = bits == 4   ? qmv_mfma_detail::launch_bits<4>(mp, compute_units(), stream)
+                           : bits == 2 ? qmv_mfma_detail::launch_bits<2>(mp, compute_units(), stream)
+                                       : qmv_mfma_detail::launch_bits<8>(mp, compute_units(), stream);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
   }
   if (forced_path() == 0 && M <= 8 && qmv_split_detail::fits(K, bits, M)) {
     qmv_split_detail::Params sp;
