@@ -40,6 +40,9 @@ bitmm_status device_check(hipStream_t) {
   return known == 1 ? BITMM_OK : BITMM_ERR_DEVICE;
 }
 
+// Largest K of the dense calls (see validate_dense): 320 * K * 2 < 2^31.
+constexpr int64_t kMaxDenseK = (int64_t)INT32_MAX / 640;
+
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 // Quantization groups along K the kernels take (each 16-byte chunk of codes lies in one).
@@ -58,6 +61,9 @@ bitmm_status validate_dense(const void* x, const uint32_t* w, const void* s, con
   if (M < 0 || N < 0 || K < 1 || K % group != 0 || K % 64 != 0) return BITMM_ERR_SHAPE;
   // Index arithmetic inside the kernels is 32-bit per dimension.
   if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX) return BITMM_ERR_SHAPE;
+  // Byte offsets into a tile of activation rows (up to 320 rows of K bf16 values) and the
+  // buffer descriptors over them are 32-bit: K * 2 * 320 must stay below 2^31.
+  if (K > kMaxDenseK) return BITMM_ERR_UNSUPPORTED;
   *empty = (M == 0 || N == 0);
   if (*empty) return BITMM_OK;
   if (!x || !w || !s || !b || !y) return BITMM_ERR_NULL;
@@ -119,11 +125,14 @@ bitmm_status bitmm_qmm(const void* x, const uint32_t* w, const void* scales, con
     const uint16_t* ss = static_cast<const uint16_t*>(scales);
     const uint16_t* bs = static_cast<const uint16_t*>(biases);
     // M*B >= 8 selects the GEMM (the engine's routing rule); below it the GEMV kernel
-    // streams W once for all rows.
-    hipError_t e = M < 8 ? bitmm::launch_qmv(xs, w, ss, bs, y, M, N, K, bits, group_size,
-                                             out == BITMM_OUT_F32, hs)
-                         : bitmm::launch_qmm_mfma(xs, w, ss, bs, y, M, N, K, bits, group_size,
-                                                  out == BITMM_OUT_F32, hs);
+    // streams W once for all rows. At M = 8 the GEMV's matrix-core form is still the
+    // faster one where it takes the shape (K = 5120, N = 13824: 17.6 against 33.9 us at
+    // 4 bits, 26.5 against 36.1 at 8), so it keeps those rows too.
+    const bool gemv = M < 8 || (M == 8 && bitmm::qmv_mfma_takes(K, bits, M));
+    hipError_t e = gemv ? bitmm::launch_qmv(xs, w, ss, bs, y, M, N, K, bits, group_size,
+                                            out == BITMM_OUT_F32, hs)
+                        : bitmm::launch_qmm_mfma(xs, w, ss, bs, y, M, N, K, bits, group_size,
+                                                 out == BITMM_OUT_F32, hs);
     return e == hipSuccess ? BITMM_OK : BITMM_ERR_LAUNCH;
   } catch (...) {
     return BITMM_ERR_LAUNCH;

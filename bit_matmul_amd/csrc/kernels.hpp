@@ -25,6 +25,9 @@ hipError_t launch_gather_qmv(const uint16_t* x, const uint32_t* w, const uint16_
                              int64_t E, int64_t T, int bits, int group, bool out_f32,
                              hipStream_t stream);
 
+// Whether the matrix-core small-M GEMV takes M rows at this K and code width (M <= 8).
+bool qmv_mfma_takes(int64_t K, int bits, int64_t M);
+
 // Matrix-core GEMM for M >= 8.
 hipError_t launch_qmm_mfma(const uint16_t* x, const uint32_t* w, const uint16_t* scales,
                            const uint16_t* biases, void* y, int64_t M, int64_t N, int64_t K,

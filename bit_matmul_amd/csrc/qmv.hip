@@ -10,8 +10,6 @@
 //   qmv_kernel (qmv_impl.hpp): up to 8 activation rows per launch, any K (several
 //     passes over K when a row does not fit), for what the others do not take (2-bit
 //     codes with K past the split kernel's range: four rows per launch).
-#include <stdlib.h>
-
 #include <atomic>
 
 #include "kernels.hpp"
@@ -23,19 +21,6 @@
 namespace bitmm {
 
 namespace {
-
-// Kernel choice: 0 = automatic, 1 = the general small-M kernel even for one row.
-// BITMM_QMV_PATH = auto | valu (comparison knob, read on every call).
-int forced_path() {
-  const char* e = getenv("BITMM_QMV_PATH");
-  return (e && e[0] == 'v') ? 1 : 0;
-}
-
-// Integer tuning knob from the environment (0 when unset).
-int env_int(const char* name) {
-  const char* e = getenv(name);
-  return e ? atoi(e) : 0;
-}
 
 // Compute units of the current device (cached per device id).
 int compute_units() {
@@ -66,7 +51,7 @@ hipError_t launch_rows(const uint16_t* x, const uint32_t* w, const uint16_t* sca
   const size_t ysz = out_f32 ? 4 : 2;
   // 2-bit codes: the decode kernel for one row, the split-K kernel for up to 3 rows (more
   // rows in launches of 3), else the general kernel (rows four at a time).
-  if (M == 1 && forced_path() == 0 && qmv_dma_detail::pick_lanes(nch) != 0) {
+  if (M == 1 && qmv_dma_detail::pick_lanes(nch) != 0) {
     qmv_dma_detail::Params dp;
     dp.x = x;
     dp.w = w;
@@ -79,14 +64,12 @@ hipError_t launch_rows(const uint16_t* x, const uint32_t* w, const uint16_t* sca
     dp.out_f32 = out_f32 ? 1 : 0;
     dp.steps_per_wave = dp.total_steps = 0;
     dp.bt = bt;
-    // BITMM_QMV_WAVES_PER_CU: launch-shape tuning knob (0 = the built-in target).
-    const int wpc = env_int("BITMM_QMV_WAVES_PER_CU");
-    return bits == 4   ? qmv_dma_detail::launch_bits<4>(dp, compute_units(), wpc, stream)
-           : bits == 2 ? qmv_dma_detail::launch_bits<2>(dp, compute_units(), wpc, stream)
-                       : qmv_dma_detail::launch_bits<8>(dp, compute_units(), wpc, stream);
+    return bits == 4   ? qmv_dma_detail::launch_bits<4>(dp, compute_units(), 0, stream)
+           : bits == 2 ? qmv_dma_detail::launch_bits<2>(dp, compute_units(), 0, stream)
+                       : qmv_dma_detail::launch_bits<8>(dp, compute_units(), 0, stream);
   }
   // Dense calls with several rows: the matrix-core GEMV, eight rows per launch.
-  if (forced_path() == 0 && bt.exp == nullptr && M >= 2 && qmv_mfma_detail::fits(K, bits, M < 8 ? M : 8)) {
+  if (bt.exp == nullptr && M >= 2 && qmv_mfma_detail::fits(K, bits, M < 8 ? M : 8)) {
     for (int64_t m0 = 0; m0 < M; m0 += 8) {
       qmv_mfma_detail::Params mp;
       mp.x = x + m0 * K;
@@ -108,7 +91,7 @@ hipError_t launch_rows(const uint16_t* x, const uint32_t* w, const uint16_t* sca
     }
     return hipSuccess;
   }
-  if (forced_path() == 0 && M <= 8 && qmv_split_detail::fits(K, bits, M)) {
+  if (M <= 8 && qmv_split_detail::fits(K, bits, M)) {
     qmv_split_detail::Params sp;
     sp.x = x;
     sp.w = w;
@@ -126,7 +109,7 @@ hipError_t launch_rows(const uint16_t* x, const uint32_t* w, const uint16_t* sca
   }
   // 2-bit codes beyond 3 rows: launches of up to 3 rows on the kernels above (the split
   // kernel takes 3 rows in about 40 % of the time the general kernel needs for 4).
-  if (bits == 2 && M > 3 && forced_path() == 0 && qmv_split_detail::fits(K, 2, 3)) {
+  if (bits == 2 && M > 3 && qmv_split_detail::fits(K, 2, 3)) {
     for (int64_t m0 = 0; m0 < M; m0 += 3) {
       const int64_t mr = M - m0 < 3 ? M - m0 : 3;
       const hipError_t e = launch_rows(x + m0 * K, w, scales, biases, static_cast<char*>(y) + (size_t)(m0 * N) * ysz,
@@ -164,6 +147,8 @@ hipError_t launch_rows(const uint16_t* x, const uint32_t* w, const uint16_t* sca
 }
 
 }  // namespace
+
+bool qmv_mfma_takes(int64_t K, int bits, int64_t M) { return qmv_mfma_detail::fits(K, bits, M); }
 
 hipError_t launch_qmv(const uint16_t* x, const uint32_t* w, const uint16_t* scales,
                       const uint16_t* biases, void* y, int64_t M, int64_t N, int64_t K, int bits,

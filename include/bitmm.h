@@ -32,10 +32,10 @@
  *
  * Precision. Accumulation is always f32 (the pages' decode fix, PR #1539 in the
  * epic's sub-issue list, is to stop accumulating the 4-bit GEMV in bf16).
- *   - bitmm_qmv, and bitmm_qmm for M < 8: every product x*w is formed exactly (the
- *     code enters as an exact bf16 integer and the group scale is applied in f32).
- *     2-bit codes take the general GEMV kernel, four activation rows per launch.
- *   - bitmm_qmm for M >= 8 and bitmm_gather_qmm: w = fma(s, q, b) in f32 is rounded
+ *   - bitmm_qmv, and bitmm_qmm on the GEMV kernels (M < 8, and M = 8 where the
+ *     matrix-core GEMV takes it): every product x*w is formed exactly (the code enters
+ *     as an exact bf16 integer and the group scale is applied in f32).
+ *   - bitmm_qmm on the matrix-core GEMM and bitmm_gather_qmm: w = fma(s, q, b) in f32 is rounded
  *     to bf16 and multiplied on the matrix cores (a dense bf16 GEMM after
  *     dequantization, as the grouped path on the pages is), f32 accumulate.
  *
@@ -108,6 +108,8 @@ const char* bitmm_status_string(bitmm_status s);
  *   checkpoint is group 64; its diagnosis item 4 quotes a tile rule keyed on
  *   group_size <= 64, so other group sizes exist in the format); K a multiple of 64 and
  *   of group_size.
+ * Limit (else BITMM_ERR_UNSUPPORTED): K <= 3355443 (byte offsets within a tile of up to 320
+ * activation rows are 32-bit: 320 * K * 2 < 2^31). Same for bitmm_qmm.
  */
 bitmm_status bitmm_qmv(const void* x, const uint32_t* w, const void* scales, const void* biases,
                        void* y, int64_t M, int64_t N, int64_t K, int bits, int group_size,
@@ -116,8 +118,10 @@ bitmm_status bitmm_qmv(const void* x, const uint32_t* w, const void* scales, con
 /*
  * Prefill GEMM: same operation and arguments as bitmm_qmv, for any M. Following the
  * engine's routing rule quoted in issue #1538 (the first 2026-08-31 comment: M*B >= 8
- * selects the GEMM), M < 8 runs the GEMV kernel (the small-M path) and M >= 8 the
- * matrix-core kernel.
+ * selects the GEMM), M < 8 runs the GEMV kernel (the small-M path) and M > 8 the
+ * matrix-core GEMM; M = 8 stays on the GEMV where its matrix-core form takes the shape
+ * (K <= 16384 at 4 bits, 8192 at 8, 32768 at 2), which is faster there. The choice of
+ * kernel never changes what is computed.
  */
 bitmm_status bitmm_qmm(const void* x, const uint32_t* w, const void* scales, const void* biases,
                        void* y, int64_t M, int64_t N, int64_t K, int bits, int group_size,

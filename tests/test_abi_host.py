@@ -100,6 +100,8 @@ DENSE_CASES = [
     (dict(M=-1), bm.BITMM_ERR_SHAPE),
     (dict(N=-5), bm.BITMM_ERR_SHAPE),
     (dict(M=1 << 31), bm.BITMM_ERR_SHAPE),
+    (dict(K=3355456), bm.BITMM_ERR_UNSUPPORTED),   # 320 * K * 2 >= 2^31 (32-bit tile offsets)
+    (dict(K=3355392), None),                       # the largest multiple of 64 below the limit
     (dict(M=0), bm.BITMM_OK),                      # empty problem: nothing enqueued
     (dict(N=0), bm.BITMM_OK),
     (dict(M=0, x=0, y=0), bm.BITMM_OK),            # pointers unused when empty

@@ -63,12 +63,12 @@ def test_gather_qmv_random(T, B, E, N, K, tokens, out, bits):
     G.assert_close(run(g, out), ref(g), out, f"gather_qmv T{T} B{B} E{E} N{N} K{K} b{bits}")
 
 
-@pytest.mark.parametrize("bits", [4, 8])
-def test_gather_qmv_general_kernel_forced(bits, monkeypatch):
-    """The general small-M kernel, forced with the BITMM_QMV_PATH knob, on gathered rows."""
-    monkeypatch.setenv("BITMM_QMV_PATH", "valu")
-    g = I.random_indexed(3, 10, 5, 77, 2816, bits, seed=bits)
-    G.assert_close(run(g, "f32"), ref(g), "f32", "forced general kernel")
+@pytest.mark.parametrize("bits,K", [(4, 24576), (8, 12288), (2, 24576)])
+def test_gather_qmv_general_kernel(bits, K):
+    """Gathered rows with K past the decode and split-K kernels' range: the general
+    kernel."""
+    g = I.random_indexed(3, 10, 5, 77, K, bits, seed=bits)
+    G.assert_close(run(g, "f32"), ref(g), "f32", f"general kernel b{bits} K{K}")
 
 
 @pytest.mark.parametrize("bits", [4, 8])

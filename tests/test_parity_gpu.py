@@ -51,18 +51,22 @@ def test_qmv_small(M, N, K, bits, out):
     G.assert_close(got, oracle_dense(d), out, f"qmv M{M} N{N} K{K} b{bits}")
 
 
-@pytest.mark.parametrize("path", ["auto", "valu"])
-@pytest.mark.parametrize("bits", [4, 8])
-@pytest.mark.parametrize("M,N,K", [(1, 300, 640), (1, 64, 8256), (1, 33, 192), (3, 130, 5120),
-                                   (8, 40, 576)])
-def test_qmv_every_kernel(M, N, K, bits, path, monkeypatch):
-    """Both GEMV kernel forms (the one-row LDS-staged kernel where it applies, and the
-    general small-M kernel forced with the BITMM_QMV_PATH knob) against the oracle,
-    f32 output, where the exact-product rule applies."""
-    monkeypatch.setenv("BITMM_QMV_PATH", path)
+# Every GEMV kernel form, reached through the shapes that select it (one row: the decode
+# kernel up to K = 10240 at 4 bits and 5120 at 8, then the split-K kernel up to 16384 and
+# 8192, then the general kernel; 2 to 8 rows: the matrix-core GEMV up to K = 16384 and
+# 8192, then the general kernel).
+EVERY_KERNEL = [(1, 300, 640, 4), (1, 33, 192, 8), (1, 200, 12288, 4), (1, 200, 6144, 8),
+                (1, 100, 20480, 4), (1, 100, 10240, 8), (3, 130, 20480, 4), (6, 50, 10240, 8),
+                (3, 130, 5120, 4), (8, 40, 576, 8)]
+
+
+@pytest.mark.parametrize("M,N,K,bits", EVERY_KERNEL)
+def test_qmv_every_kernel(M, N, K, bits):
+    """Each GEMV kernel form against the oracle, f32 output, where the exact-product rule
+    applies."""
     d = I.random_dense(M, N, K, bits, seed=11 * M + N + K)
     got = G.to_f64(G.run_dense("bitmm_qmv", d, "f32"))
-    G.assert_close(got, oracle_dense(d), "f32", f"qmv[{path}] M{M} N{N} K{K} b{bits}")
+    G.assert_close(got, oracle_dense(d), "f32", f"qmv M{M} N{N} K{K} b{bits}")
 
 
 # The LDS-ring GEMV at its layout edges: one row; R-row steps with a ragged last
@@ -73,23 +77,22 @@ def test_qmv_every_kernel(M, N, K, bits, path, monkeypatch):
 @pytest.mark.parametrize("out", ["bf16", "f32"])
 @pytest.mark.parametrize("N,K", [(1, 64), (5, 5120), (4099, 5120), (257, 512), (33, 192),
                                  (2048, 10240), (100, 2816), (3001, 1344)])
-def test_qmv_dma_layouts(N, K, bits, out, monkeypatch):
-    monkeypatch.setenv("BITMM_QMV_PATH", "auto")
+def test_qmv_dma_layouts(N, K, bits, out):
     d = I.random_dense(1, N, K, bits, seed=N + 3 * K + bits)
     got = G.to_f64(G.run_dense("bitmm_qmv", d, out))
     G.assert_close(got, oracle_dense(d), out, f"qmv[dma] N{N} K{K} b{bits}")
 
 
 @pytest.mark.parametrize("bits", [2, 4, 8])
-@pytest.mark.parametrize("wpc", [1, 4, 8])
-def test_qmv_dma_steps_per_wave(wpc, bits, monkeypatch):
-    """The decode kernel with several steps per wave (the launch target set low: 8, 4 or 2
-    consecutive steps per wave, straight-line code with up to four steps in flight),
-    including a ragged last wave."""
-    monkeypatch.setenv("BITMM_QMV_WAVES_PER_CU", str(wpc))
-    d = I.random_dense(1, 4099 * 2 + 1, 1024, bits, seed=wpc + bits)
+@pytest.mark.parametrize("N", [65539, 131075, 262147])
+def test_qmv_dma_steps_per_wave(N, bits):
+    """The decode kernel with several steps per wave: at K = 256 a step is four rows at 2
+    and 4 bits (two at 8), and past 16384, 32768 and 65536 steps each wave owns 2, 4 and 8
+    consecutive steps (straight-line code with up to four steps in flight); N leaves a
+    ragged last step and a ragged last wave."""
+    d = I.random_dense(1, N, 256, bits, seed=N + bits)
     got = G.to_f64(G.run_dense("bitmm_qmv", d, "f32"))
-    G.assert_close(got, oracle_dense(d), "f32", f"qmv[dma] wpc{wpc} b{bits}")
+    G.assert_close(got, oracle_dense(d), "f32", f"qmv[dma] N{N} b{bits}")
 
 
 @pytest.mark.parametrize("bits", [4, 8])
@@ -310,10 +313,14 @@ def test_tiny_qmv_full():
 
 
 @pytest.mark.parametrize("M,N,bits", FULL_DENSE)
-def test_hidden5120_sampled(M, N, bits):
+def test_hidden5120_full_size(M, N, bits):
+    """The hidden-5120 workloads at their real sizes: every output of the decode GEMV and
+    of the 3-row GEMM against the oracle; the 600-row GEMM (42 G multiply-adds for the
+    oracle) on sampled outputs plus its corners and last row and column."""
     d = I.hidden5120(M, N, bits)
     fn = "bitmm_qmv" if M == 1 else "bitmm_qmm"
     exact_path = M < 8
+    ref_all = oracle_dense(d) if M < 8 else None
     for out in (("bf16", "f32") if exact_path else ("bf16",)):
         y = G.run_dense(fn, d, out)
         y2 = G.run_dense(fn, d, out)
@@ -321,13 +328,16 @@ def test_hidden5120_sampled(M, N, bits):
         assert t.equal(y, y2), "not deterministic"
         got = G.to_f64(y)
         assert np.all(np.isfinite(got))
-        r, c = G.sample_points(d.M, d.N, 3000, seed=M + N)
-        ref = oracle.qmm_points(d.x, d.w, d.scales, d.biases, r, c, bits)
-        G.assert_close(got[r, c], ref, out, f"{d.name} {out}")
+        if ref_all is not None:
+            G.assert_close(got, ref_all, out, f"{d.name} {out}")
+        else:
+            r, c = G.sample_points(d.M, d.N, 3000, seed=M + N)
+            ref = oracle.qmm_points(d.x, d.w, d.scales, d.biases, r, c, bits)
+            G.assert_close(got[r, c], ref, out, f"{d.name} {out}")
 
 
 @pytest.mark.parametrize("which", ["up", "down"])
-def test_moe_gather_sampled(which):
+def test_moe_gather_full_size(which):
     g = I.moe_gather(which)
     y, ws = G.run_gather(g, "bf16")
     y2, _ = G.run_gather(g, "bf16")
@@ -336,9 +346,9 @@ def test_moe_gather_sampled(which):
     wsn = ws.cpu().numpy().view(np.uint32)
     assert wsn[0] == 0
     got = G.to_f64(y)
-    r, c = G.sample_points(g.B, g.N, 3000, seed=5)
-    ref = oracle.gather_qmm_points(g.x, g.w, g.scales, g.biases, g.expert_idx, r, c, g.bits)
-    G.assert_close(got[r, c], ref, "bf16", g.name)
+    # every output (9.1 G multiply-adds for the oracle, a few seconds on the host cores)
+    ref = oracle.gather_qmm(g.x, g.w, g.scales, g.biases, g.expert_idx, g.bits)
+    G.assert_close(got, ref, "bf16", g.name)
 
 
 # ---------------------------------------------------------------------------

@@ -27,6 +27,9 @@ def _gpu():
 
 SHAPES = [(1, 300, 1024), (1, 70, 5120), (3, 133, 2048), (2, 61, 16384), (3, 45, 5120), (5, 40, 4096),
           (7, 33, 384), (1, 9, 20480),
+          # past the decode (K <= 20480), split-K and matrix-core GEMV (K <= 32768) ranges:
+          # the general kernel, one row and launches of four rows
+          (1, 37, 24576), (2, 21, 40960), (4, 19, 40960),
           (8, 70, 256), (40, 129, 1024), (300, 200, 2048), (96, 64, 2560), (70, 66, 5120)]
 
 
