@@ -92,10 +92,16 @@ typedef enum { BITMM_DTYPE_BF16 = 0, BITMM_DTYPE_F16 = 1 } bitmm_dtype;
    column, K contiguous; the MoE layer's own layout) or [K, N] (N contiguous). */
 typedef enum { BITMM_LAYOUT_NK = 0, BITMM_LAYOUT_KN = 1 } bitmm_layout;
 
-/* Version of this interface (BITMM_ABI_VERSION). */
+/* Version of this interface (BITMM_ABI_VERSION), so a caller can check what it loaded
+   before the first call. Plumbing, not an operation of the pages; its role matches the
+   capability probe of issue #1537 that epic #1536 lists under "Phase 0" (the runtime
+   asks what it is running against before choosing a path). */
 int bitmm_abi_version(void);
 
-/* Static, human-readable name of a status code ("unknown status" otherwise). */
+/* Static, human-readable name of a status code ("unknown status" otherwise). Plumbing,
+   not an operation of the pages: every failure comes back as a named status instead of
+   an opaque launch failure, as issue #1538, comment "Baseline recorded: PR #1556"
+   ("Build coverage decision") credits #1537 with doing for an architecture mismatch. */
 const char* bitmm_status_string(bitmm_status s);
 
 /*
@@ -129,7 +135,10 @@ bitmm_status bitmm_qmm(const void* x, const uint32_t* w, const void* scales, con
 
 /*
  * Bytes of device workspace bitmm_gather_qmm needs for B rows, N columns and E experts
- * (a multiple of 256; 0 if an argument is negative or E < 1).
+ * (a multiple of 256; 0 if an argument is negative or E < 1): the status word and the
+ * per-expert row offsets, the data that the setup step of the grouped path produces
+ * ahead of the grouped GEMM (PR #1562, "The branch is live": prepare_grouped_mm_data,
+ * one per grouped-GEMM launch).
  */
 size_t bitmm_gather_qmm_workspace_bytes(int64_t B, int64_t N, int64_t E);
 
