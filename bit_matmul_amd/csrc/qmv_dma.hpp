@@ -47,12 +47,14 @@ struct Params {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
-// Launch target in waves per CU. At 32 every shape up to 16384 steps gets one step per
-// wave: the least arithmetic left for each wave once its codes arrive (the tail of the
-// stream). Measured against 8 (two steps per wave at N = 13824): 4-bit N = 13824
-// 10.8 -> 10.45 us, 8-bit 17.2 -> 13.6 us, 8-bit N = 5120 7.6 -> 7.1 us, MoE decode of
-// 4 tokens 10.0 -> 8.7 us (up) and 11.8 -> 11.2 us (down); 4-bit N = 5120 unchanged.
-constexpr int kWavesPerCu = 32;
+// Launch target in waves per CU. At 16, shapes from 8192 steps on give each wave two
+// steps (all of its loads issued up front: one 5 KB burst per wave at K = 5120, 4 bits)
+// and smaller ones one step. Measured on one box, same session: 4-bit N = 13824
+// 11.05 -> 10.30 us against a target of 32 (one step per wave), N = 5120, 8-bit, 2-bit
+// and the MoE decode shapes unchanged within the box's noise. A target of 8 (four steps
+// per wave at N = 13824) is slower: 10.8 us 4-bit, and earlier 17.2 against 13.6 us
+// 8-bit (more arithmetic left for each wave once its codes arrive).
+constexpr int kWavesPerCu = 16;
 
 template <int BITS, int L, int C, int SPW>
 struct Cfg {

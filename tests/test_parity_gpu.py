@@ -84,11 +84,11 @@ def test_qmv_dma_layouts(N, K, bits, out):
 
 
 @pytest.mark.parametrize("bits", [2, 4, 8])
-@pytest.mark.parametrize("N", [65539, 131075, 262147])
+@pytest.mark.parametrize("N", [32771, 65539, 131075, 262147])
 def test_qmv_dma_steps_per_wave(N, bits):
-    """The decode kernel with several steps per wave: at K = 256 a step is four rows at 2
-    and 4 bits (two at 8), and past 16384, 32768 and 65536 steps each wave owns 2, 4 and 8
-    consecutive steps (straight-line code with up to four steps in flight); N leaves a
+    """The decode kernel with several steps per wave: at K = 256 a step is four rows (16
+    lanes x one chunk each), and past 8192, 16384 and 32768 steps each wave owns 2, 4 and
+    8 consecutive steps (straight-line code with up to four steps in flight); N leaves a
     ragged last step and a ragged last wave."""
     d = I.random_dense(1, N, 256, bits, seed=N + bits)
     got = G.to_f64(G.run_dense("bitmm_qmv", d, "f32"))
