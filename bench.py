@@ -807,7 +807,7 @@ def main():
         roofline = roofline_obj("hbm", cb.bytes, cb.flops, tb, ceilings)
         tr = read_summary("counters_qmv_M1_K5120_N13824_b4", src_hash)
         roofline.update({"traffic": int(num(tr, "traffic_bytes_per_launch")) if tr and num(tr, "traffic_bytes_per_launch") else None,
-                         "kernel": "qmv_dma_kernel<4, 64, 3, 1> (K=5120, N=13824, 4-bit, M=1: one step of "
+                         "kernel": "qmv_dma_kernel<4, 64, 3, 2> (K=5120, N=13824, 4-bit, M=1: two steps of "
                                    "1 row x 64 lanes x 3 chunks per wave)",
                          "algorithmic_bytes_per_launch": cb.bytes,
                          "avg_launch_us": round(tb * 1e6, 3), "spread_pct": sb["spread_pct"]})
