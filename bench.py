@@ -802,6 +802,7 @@ def main():
         # Each kernel alone, same launch configuration, for the per-kernel roofline.
         ta, sa = stats(time_steps(torch, [ca], args.steps, args.warmup, R, markers, pa.name), args.steps)
         tb, sb = stats(time_steps(torch, [cb], args.steps, args.warmup, R, markers, pb.name), args.steps)
+        kb = bm.bitmm_last_launches()
         ta, tb = ta / 1e6, tb / 1e6
         gpu_time[pa.name], gpu_time[pb.name] = ta, tb
         roofline = roofline_obj("hbm", cb.bytes, cb.flops, tb, ceilings)
@@ -810,7 +811,8 @@ def main():
                          "kernel": "qmv_dma_kernel<4, 64, 3, 2> (K=5120, N=13824, 4-bit, M=1: two steps of "
                                    "1 row x 64 lanes x 3 chunks per wave)",
                          "algorithmic_bytes_per_launch": cb.bytes,
-                         "avg_launch_us": round(tb * 1e6, 3), "spread_pct": sb["spread_pct"]})
+                         "avg_launch_us": round(tb * 1e6, 3), "spread_pct": sb["spread_pct"],
+                         "launch": kb})
         result = {
             "metric": "qmv HBM GB/s (% of peak); qmm & MoE gather_qmm TFLOPS (% of MFMA peak)",
             "value": round(value, 1),
@@ -863,6 +865,7 @@ def main():
             t1, sp = stats(time_steps(torch, [c], steps, max(5, args.warmup // 2), R, markers, p.name), steps)
             t1 /= 1e6
             gpu_time[p.name] = t1
+            sp["kernels"] = bm.bitmm_last_launches()  # what the library enqueued for one call
             s = summarize(c, t1, p.name, bound, sp, ceilings)
             attach_profiles(s, src_hash)
             log(f"suite {p.name}: {s['us_per_launch']} us (spread {sp['spread_pct']} %), {s['GB_s']} GB/s, "

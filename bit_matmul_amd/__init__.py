@@ -47,7 +47,8 @@ BITMM_LAYOUT_KN = 1
 GROUP = 64
 
 __all__ = [
-    "BitmmError", "lib", "bitmm_abi_version", "bitmm_status_string", "bitmm_qmv", "bitmm_qmm",
+    "BitmmError", "lib", "bitmm_abi_version", "bitmm_status_string", "bitmm_last_launches",
+    "bitmm_qmv", "bitmm_qmm",
     "bitmm_gather_qmm_workspace_bytes", "bitmm_gather_qmm", "bitmm_gather_qmm_noalloc", "bitmm_gather_qmv",
     "bitmm_gather_qmm_indexed_workspace_bytes", "bitmm_gather_qmm_indexed", "qmv", "qmm",
     "gather_qmm", "gather_qmv", "gather_qmm_indexed", "bitmm_gather_mm_workspace_bytes",
@@ -82,6 +83,8 @@ def lib() -> ctypes.CDLL:
         L.bitmm_abi_version.restype = I
         L.bitmm_status_string.argtypes = [I]
         L.bitmm_status_string.restype = ctypes.c_char_p
+        L.bitmm_last_launches.argtypes = [ctypes.c_char_p, SZ]
+        L.bitmm_last_launches.restype = SZ
         dense = [P, P, P, P, P, I64, I64, I64, I, I, I, P]
         L.bitmm_qmv.argtypes = dense
         L.bitmm_qmv.restype = I
@@ -114,6 +117,14 @@ def bitmm_abi_version() -> int:
 
 def bitmm_status_string(status: int) -> str:
     return lib().bitmm_status_string(int(status)).decode()
+
+
+def bitmm_last_launches() -> list:
+    """The kernels this thread's most recent bitmm_* call enqueued, one string each."""
+    n = int(lib().bitmm_last_launches(None, 0))
+    buf = ctypes.create_string_buffer(n + 1)
+    lib().bitmm_last_launches(buf, n + 1)
+    return [line for line in buf.value.decode().split("\n") if line]
 
 
 def bitmm_gather_qmm_workspace_bytes(B: int, N: int, E: int) -> int:

@@ -6,10 +6,35 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <stdarg.h>
+#include <stdio.h>
+
 #include <atomic>
+#include <string>
 
 #include "bitmm.h"
 #include "kernels.hpp"
+
+namespace bitmm {
+
+namespace {
+thread_local std::string t_launches;  // this thread's kernel-choice record
+}
+
+void launch_log_begin() { t_launches.clear(); }
+
+void launch_log(dim3 grid, dim3 block, size_t lds_bytes, const char* fmt, ...) {
+  char name[256];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(name, sizeof name, fmt, ap);
+  va_end(ap);
+  char line[384];
+  snprintf(line, sizeof line, "%s grid=%ux%u block=%u lds=%zu\n", name, grid.x, grid.y, block.x, lds_bytes);
+  t_launches += line;
+}
+
+}  // namespace bitmm
 
 namespace {
 
@@ -79,6 +104,16 @@ extern "C" {
 
 int bitmm_abi_version(void) { return BITMM_ABI_VERSION; }
 
+size_t bitmm_last_launches(char* buf, size_t len) {
+  const std::string& s = bitmm::t_launches;
+  if (buf && len > 0) {
+    const size_t n = s.size() < len - 1 ? s.size() : len - 1;
+    memcpy(buf, s.data(), n);
+    buf[n] = '\0';
+  }
+  return s.size();
+}
+
 const char* bitmm_status_string(bitmm_status s) {
   switch (s) {
     case BITMM_OK: return "ok";
@@ -97,6 +132,7 @@ bitmm_status bitmm_qmv(const void* x, const uint32_t* w, const void* scales, con
                        void* y, int64_t M, int64_t N, int64_t K, int bits, int group_size,
                        bitmm_out out, void* stream) {
   try {
+    bitmm::launch_log_begin();
     bool empty = false;
     bitmm_status st = validate_dense(x, w, scales, biases, y, M, N, K, bits, group_size, out, &empty);
     if (st != BITMM_OK || empty) return st;
@@ -116,6 +152,7 @@ bitmm_status bitmm_qmm(const void* x, const uint32_t* w, const void* scales, con
                        void* y, int64_t M, int64_t N, int64_t K, int bits, int group_size,
                        bitmm_out out, void* stream) {
   try {
+    bitmm::launch_log_begin();
     bool empty = false;
     bitmm_status st = validate_dense(x, w, scales, biases, y, M, N, K, bits, group_size, out, &empty);
     if (st != BITMM_OK || empty) return st;
@@ -150,6 +187,7 @@ bitmm_status bitmm_gather_qmm(const void* x, const uint32_t* w, const void* scal
                               bitmm_out out, void* workspace, size_t workspace_bytes,
                               void* stream) {
   try {
+    bitmm::launch_log_begin();
     if (!group_ok(group_size) || !bits_ok(bits, group_size)) return BITMM_ERR_UNSUPPORTED;
     if (out != BITMM_OUT_BF16 && out != BITMM_OUT_F32) return BITMM_ERR_UNSUPPORTED;
     if (B < 0 || N < 0 || K < 1 || E < 1 || K % group_size != 0 || K % 64 != 0) return BITMM_ERR_SHAPE;
@@ -182,6 +220,7 @@ bitmm_status bitmm_gather_qmm_noalloc(const void* x, const uint32_t* w, const vo
                                       int group_size, bitmm_out out, uint32_t* status,
                                       void* stream) {
   try {
+    bitmm::launch_log_begin();
     if (!group_ok(group_size) || !bits_ok(bits, group_size)) return BITMM_ERR_UNSUPPORTED;
     if (out != BITMM_OUT_BF16 && out != BITMM_OUT_F32) return BITMM_ERR_UNSUPPORTED;
     if (B < 0 || N < 0 || K < 1 || E < 1 || K % group_size != 0 || K % 64 != 0) return BITMM_ERR_SHAPE;
@@ -219,6 +258,7 @@ bitmm_status bitmm_gather_qmm_indexed(const void* x, const uint32_t* w, const vo
                                       bitmm_out out, void* workspace, size_t workspace_bytes,
                                       void* stream) {
   try {
+    bitmm::launch_log_begin();
     if (!group_ok(group_size) || !bits_ok(bits, group_size)) return BITMM_ERR_UNSUPPORTED;
     if (out != BITMM_OUT_BF16 && out != BITMM_OUT_F32) return BITMM_ERR_UNSUPPORTED;
     if (B < 0 || N < 0 || T < 0 || K < 1 || E < 1 || K % group_size != 0 || K % 64 != 0) return BITMM_ERR_SHAPE;
@@ -254,6 +294,7 @@ bitmm_status bitmm_gather_qmv(const void* x, const uint32_t* w, const void* scal
                               int64_t E, int64_t T, int bits, int group_size, bitmm_out out,
                               void* stream) {
   try {
+    bitmm::launch_log_begin();
     if (!group_ok(group_size) || !bits_ok(bits, group_size)) return BITMM_ERR_UNSUPPORTED;
     if (out != BITMM_OUT_BF16 && out != BITMM_OUT_F32) return BITMM_ERR_UNSUPPORTED;
     if (B < 0 || N < 0 || T < 0 || K < 1 || E < 1 || K % group_size != 0 || K % 64 != 0) return BITMM_ERR_SHAPE;
@@ -288,6 +329,7 @@ bitmm_status bitmm_gather_mm(const void* x, const void* w, const int32_t* token_
                              int64_t E, int64_t T, bitmm_dtype dtype, bitmm_layout layout,
                              bitmm_out out, void* workspace, size_t workspace_bytes, void* stream) {
   try {
+    bitmm::launch_log_begin();
     if (dtype != BITMM_DTYPE_BF16 && dtype != BITMM_DTYPE_F16) return BITMM_ERR_UNSUPPORTED;
     if (layout != BITMM_LAYOUT_NK && layout != BITMM_LAYOUT_KN) return BITMM_ERR_UNSUPPORTED;
     if (out != BITMM_OUT_BF16 && out != BITMM_OUT_F32 && out != BITMM_OUT_F16)

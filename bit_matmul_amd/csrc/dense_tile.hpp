@@ -25,6 +25,10 @@
 // bring from past K (the next row, or zeros past the tensor) are never multiplied.
 #pragma once
 
+#include <stdio.h>
+
+#include <string>
+
 #include "common.hpp"
 #include "tile_epilogue.hpp"
 
@@ -55,6 +59,16 @@ struct MmTileD {
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
   static_assert(WAVES * BM * 64 <= LDS_BYTES, "epilogue scratch");
   static_assert((NS - 2) * C <= 63, "vmcnt range");
+
+  // The template arguments as text (host side, for the kernel-choice record).
+  static const char* name() {
+    static const std::string s = [] {
+      char b[96];
+      snprintf(b, sizeof b, "MmTileD<%d, %d, %d, %d, %d>", DT, LAYOUT, MB, KS, NS);
+      return std::string(b);
+    }();
+    return s.c_str();
+  }
 
   __device__ static __forceinline__ f32x16_t mfma(u32x4_t a, u32x4_t b, f32x16_t c) {
     if constexpr (DT == 0)

@@ -242,6 +242,8 @@ hipError_t launch_indexed(GatherParams p, hipStream_t stream) {
   p.tiles_n = (p.N + T::BN - 1) / T::BN;
   hipLaunchKernelGGL((gather_qmm_indexed_kernel<BITS, T>), dim3(p.E * p.tiles_n), dim3(T::THREADS), 0,
                      stream, p);
+  launch_log(dim3(p.E * p.tiles_n), dim3(T::THREADS), T::LDS_BYTES, "gather_qmm_indexed_kernel<%d, %s>",
+             BITS, T::name());
   return hipGetLastError();
 }
 
@@ -250,6 +252,8 @@ hipError_t launch_grouped(GatherParams p, hipStream_t stream) {
   p.tiles_n = (p.N + T::BN - 1) / T::BN;
   hipLaunchKernelGGL((gather_qmm_kernel<BITS, T>), dim3(p.E * p.tiles_n), dim3(T::THREADS), 0,
                      stream, p);
+  launch_log(dim3(p.E * p.tiles_n), dim3(T::THREADS), T::LDS_BYTES, "gather_qmm_kernel<%d, %s>", BITS,
+             T::name());
   return hipGetLastError();
 }
 
@@ -356,6 +360,7 @@ hipError_t launch_gather_qmm(const uint16_t* x, const uint32_t* w, const uint16_
   uint32_t* ws = static_cast<uint32_t*>(workspace);
   hipLaunchKernelGGL(gather_prepare_kernel, dim3(1), dim3(kPrepThreads), 0, stream, expert_idx,
                      (int)B, (int)E, ws, status);
+  launch_log(dim3(1), dim3(kPrepThreads), sizeof(int), "gather_prepare_kernel");
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   GatherParams p;
@@ -392,6 +397,8 @@ hipError_t launch_gather_sort(const int32_t* token_idx, const int32_t* expert_id
   hipLaunchKernelGGL(gather_sort_kernel, dim3(1), dim3(kPrepThreads), 0, stream, token_idx,
                      expert_idx, (int)B, (int)E, (int)T, (int)N, ysz, y,
                      static_cast<uint32_t*>(workspace));
+  launch_log(dim3(1), dim3(kPrepThreads), (kMaxIndexedExperts + 1 + kPrepThreads + 1) * sizeof(int),
+             "gather_sort_kernel");
   return hipGetLastError();
 }
 

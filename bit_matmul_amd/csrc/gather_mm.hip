@@ -50,6 +50,7 @@ hipError_t launch_tiles(GmmParams p, hipStream_t stream) {
   p.tiles_n = (p.N + Tile::BN - 1) / Tile::BN;
   hipLaunchKernelGGL((gather_mm_kernel<Tile>), dim3(p.E * p.tiles_n), dim3(Tile::THREADS), 0, stream,
                      p);
+  launch_log(dim3(p.E * p.tiles_n), dim3(Tile::THREADS), Tile::LDS_BYTES, "gather_mm_kernel<%s>", Tile::name());
   return hipGetLastError();
 }
 

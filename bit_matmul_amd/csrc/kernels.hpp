@@ -11,6 +11,13 @@ namespace bitmm {
 // Output element types of the matrix-core epilogue (bitmm_out's values).
 enum OutType { kOutBf16 = 0, kOutF32 = 1, kOutF16 = 2 };
 
+// Kernel-choice record of the calling thread (bitmm_last_launches): each C-ABI call
+// starts an empty record, and every launch site appends one line naming the kernel it
+// enqueued, with its template arguments, grid, workgroup size and LDS bytes.
+void launch_log_begin();
+void launch_log(dim3 grid, dim3 block, size_t lds_bytes, const char* fmt, ...)
+    __attribute__((format(printf, 4, 5)));
+
 // GEMV / small-M path: y[M, N] = x[M, K] * dequant(w)^T, rows taken 8 at a time.
 hipError_t launch_qmv(const uint16_t* x, const uint32_t* w, const uint16_t* scales,
                       const uint16_t* biases, void* y, int64_t M, int64_t N, int64_t K, int bits,

@@ -34,6 +34,10 @@
 // + (b - 64 s); rounded to bf16 for the MFMA; f32 accumulation.
 #pragma once
 
+#include <stdio.h>
+
+#include <string>
+
 #include "common.hpp"
 #include "tile_epilogue.hpp"
 
@@ -101,6 +105,17 @@ struct MmTile4 {
   }
   static_assert(PD * WL + XD * XC <= 63, "vmcnt range");
   static_assert(WAVES * BM * 64 <= NB * XB, "epilogue staging fits in the activation buffers");
+
+  // The template arguments as text (host side, for the kernel-choice record).
+  static const char* name() {
+    static const std::string s = [] {
+      char b[128];
+      snprintf(b, sizeof b, "MmTile4<%d, %d, %d, %d, %d, %d, %d, %s, %s>", BITS, MB, WN, PD, XD, SBM, GMAX,
+               RMAP ? "true" : "false", WS ? "true" : "false");
+      return std::string(b);
+    }();
+    return s.c_str();
+  }
 
   // Byte offset of 16-byte chunk c of row r in a 128-byte-row tile: rows in blocks of
   // 16 (2 KB), row r of a block at (r & 7) * 256 + (r >> 3) * 128, chunk c at

@@ -41,6 +41,7 @@ hipError_t launch_tiles(QmmParams p, hipStream_t stream) {
   p.tiles_n = (p.N + T::BN - 1) / T::BN;
   hipLaunchKernelGGL((qmm_mfma_kernel<T>), dim3(p.tiles_m * p.tiles_n), dim3(T::THREADS), 0,
                      stream, p);
+  launch_log(dim3(p.tiles_m * p.tiles_n), dim3(T::THREADS), T::LDS_BYTES, "qmm_mfma_kernel<%s>", T::name());
   return hipGetLastError();
 }
 

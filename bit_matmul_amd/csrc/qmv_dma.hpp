@@ -27,6 +27,7 @@
 #pragma once
 
 #include "common.hpp"
+#include "kernels.hpp"
 
 namespace bitmm {
 namespace qmv_dma_detail {
@@ -345,6 +346,8 @@ hipError_t launch(Params p, hipStream_t stream) {
   const int blocks = (waves + kWaves - 1) / kWaves;
   hipLaunchKernelGGL((qmv_dma_kernel<BITS, L, C, SPW>), dim3(blocks, gemv_grid_rows(p.bt)), dim3(kThreads), 0,
                      stream, p);
+  launch_log(dim3(blocks, gemv_grid_rows(p.bt)), dim3(kThreads), T::LDS_BYTES, "qmv_dma_kernel<%d, %d, %d, %d>",
+             BITS, L, C, SPW);
   return hipGetLastError();
 }
 

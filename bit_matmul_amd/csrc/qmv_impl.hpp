@@ -20,6 +20,7 @@
 #pragma once
 
 #include "common.hpp"
+#include "kernels.hpp"
 
 namespace bitmm {
 namespace qmv_detail {
@@ -229,6 +230,8 @@ hipError_t launch_one(const QmvParams& p, hipStream_t stream) {
   const int blocks = (waves + kQmvWaves - 1) / kQmvWaves;
   hipLaunchKernelGGL((qmv_kernel<BITS, MR, RPW, CPL>), dim3(blocks, gemv_grid_rows(p.bt)),
                      dim3(kQmvThreads), 0, stream, p);
+  launch_log(dim3(blocks, gemv_grid_rows(p.bt)), dim3(kQmvThreads), 0, "qmv_kernel<%d, %d, %d, %d>", BITS,
+             MR, RPW, CPL);
   return hipGetLastError();
 }
 

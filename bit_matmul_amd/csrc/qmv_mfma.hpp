@@ -40,6 +40,7 @@
 #include <algorithm>
 
 #include "common.hpp"
+#include "kernels.hpp"
 
 namespace bitmm {
 namespace qmv_mfma_detail {
@@ -376,6 +377,8 @@ hipError_t launch(const Params& p, hipStream_t stream) {
     hipLaunchKernelGGL((qmv_mfma_kernel<BITS, C, SPW, D, 1, MG>), dim3(grid), dim3(64 * nw), lds, stream, p);
   else
     hipLaunchKernelGGL((qmv_mfma_kernel<BITS, C, SPW, D, 2, MG>), dim3(grid), dim3(64 * nw), lds, stream, p);
+  launch_log(dim3(grid), dim3(64 * nw), lds, "qmv_mfma_kernel<%d, %d, %d, %d, %d, %d>", BITS, C, SPW, D,
+             stage > kMaxStageBytes ? 0 : (wide ? 1 : 2), MG);
   return hipGetLastError();
 }
 

@@ -30,6 +30,7 @@
 #include <atomic>
 
 #include "common.hpp"
+#include "kernels.hpp"
 
 namespace bitmm {
 namespace qmv_split_detail {
@@ -315,6 +316,8 @@ hipError_t launch_s(const Params& p, hipStream_t stream) {
   const int grid = std::max(1, std::min(nblk, resident_blocks<BITS, MR, S>(nw) / (int)rows));
   hipLaunchKernelGGL((qmv_split_kernel<BITS, MR, S, max_waves(MR, BITS)>), dim3(grid, rows), dim3(64 * nw), 0,
                      stream, p);
+  launch_log(dim3(grid, rows), dim3(64 * nw), 0, "qmv_split_kernel<%d, %d, %d, %d>", BITS, MR, S,
+             max_waves(MR, BITS));
   return hipGetLastError();
 }
 

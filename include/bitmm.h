@@ -62,7 +62,7 @@
 extern "C" {
 #endif
 
-#define BITMM_ABI_VERSION 1
+#define BITMM_ABI_VERSION 2
 
 typedef enum {
   BITMM_OK = 0,
@@ -103,6 +103,19 @@ int bitmm_abi_version(void);
    an opaque launch failure, as issue #1538, comment "Baseline recorded: PR #1556"
    ("Build coverage decision") credits #1537 with doing for an architecture mismatch. */
 const char* bitmm_status_string(bitmm_status s);
+
+/*
+ * Kernel-choice record: the kernels the calling thread's most recent bitmm_qmv, bitmm_qmm,
+ * bitmm_gather_* call enqueued, one line each, "<kernel><template arguments> grid=XxY
+ * block=T lds=B" (LDS bytes the kernel declares), in launch order; empty when that call
+ * enqueued nothing (an error, or an empty problem). Copies at most len - 1 bytes and a
+ * terminating NUL into buf (nothing if buf is NULL or len is 0) and returns the record's
+ * full length. Host-only: no HIP call, no synchronisation. It names what the library
+ * chose by shape, code width, group size and alignment (the pages' engine logs its
+ * architecture decision for the same reason: epic #1536, "GB10 (sm_121) continuation",
+ * the MLXCEL_TRACE_ARCH criterion of #1537).
+ */
+size_t bitmm_last_launches(char* buf, size_t len);
 
 /*
  * Decode GEMV: y[M, N] = x[M, K] * dequant(w)^T, streaming W once per call for all M

@@ -43,13 +43,27 @@ def gpu_present():
 
 def test_exports_every_declared_function(L):
     names = header_functions()
-    assert set(names) == {"bitmm_abi_version", "bitmm_status_string", "bitmm_qmv", "bitmm_qmm",
+    assert set(names) == {"bitmm_abi_version", "bitmm_status_string", "bitmm_last_launches",
+                          "bitmm_qmv", "bitmm_qmm",
                           "bitmm_gather_qmm_workspace_bytes", "bitmm_gather_qmm",
                           "bitmm_gather_qmm_noalloc", "bitmm_gather_qmv", "bitmm_gather_qmm_indexed_workspace_bytes",
                           "bitmm_gather_qmm_indexed", "bitmm_gather_mm_workspace_bytes",
                           "bitmm_gather_mm"}
     for n in names:
         assert hasattr(L, n), f"libbitmm.so does not export {n}"
+
+
+def test_launch_record_is_empty_after_a_rejected_call(L):
+    """Every call starts a fresh kernel-choice record; a call rejected by validation (here
+    a code width the library does not take) enqueues nothing and leaves it empty. The
+    query copies nothing into a NULL or zero-length buffer and returns the full length."""
+    assert L.bitmm_qmv(*dense_args(bits=3)) == bm.BITMM_ERR_UNSUPPORTED
+    assert bm.bitmm_last_launches() == []
+    buf = ctypes.create_string_buffer(b"xyz", 4)
+    assert L.bitmm_last_launches(buf, 0) == 0
+    assert buf.value == b"xyz"
+    assert L.bitmm_last_launches(None, 16) == 0
+    assert L.bitmm_last_launches(buf, 4) == 0 and buf.value == b""
 
 
 def test_abi_version_matches_header(L):
