@@ -230,8 +230,11 @@ struct MmTile4 {
                                                    rw, woff + v * 16, gc * GB, 0));
       }
       if constexpr (SBM == 0) {
-        r.s = __builtin_amdgcn_raw_buffer_load_b16(rs, soff, gidx_uniform(gc) * 2, 0);
-        r.b = __builtin_amdgcn_raw_buffer_load_b16(rb, soff, gidx_uniform(gc) * 2, 0);
+        // Scalar offset forced into an SGPR: built in a VGPR, each load would sit in a
+        // waterfall loop.
+        const int so = __builtin_amdgcn_readfirstlane(gidx_uniform(gc) * 2);
+        r.s = __builtin_amdgcn_raw_buffer_load_b16(rs, soff, so, 0);
+        r.b = __builtin_amdgcn_raw_buffer_load_b16(rb, soff, so, 0);
       }
     };
     // WS, 4 bits: groups ge, ge+1 (ge even) of rows 0-15 and 16-31 (one 64-byte span per
@@ -246,10 +249,12 @@ struct MmTile4 {
       r0.q[0] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rw, (wsx + go) | past, 0, 0));
       r1.q[0] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rw, (wsy + go) | past, 0, 0));
       if constexpr (SBM == 0) {
-        r0.s = __builtin_amdgcn_raw_buffer_load_b16(rs, soff, gidx_uniform(min(ge, G - 1)) * 2, 0);
-        r0.b = __builtin_amdgcn_raw_buffer_load_b16(rb, soff, gidx_uniform(min(ge, G - 1)) * 2, 0);
-        r1.s = __builtin_amdgcn_raw_buffer_load_b16(rs, soff, gidx_uniform(min(ge + 1, G - 1)) * 2, 0);
-        r1.b = __builtin_amdgcn_raw_buffer_load_b16(rb, soff, gidx_uniform(min(ge + 1, G - 1)) * 2, 0);
+        const int so0 = __builtin_amdgcn_readfirstlane(gidx_uniform(min(ge, G - 1)) * 2);
+        const int so1 = __builtin_amdgcn_readfirstlane(gidx_uniform(min(ge + 1, G - 1)) * 2);
+        r0.s = __builtin_amdgcn_raw_buffer_load_b16(rs, soff, so0, 0);
+        r0.b = __builtin_amdgcn_raw_buffer_load_b16(rb, soff, so0, 0);
+        r1.s = __builtin_amdgcn_raw_buffer_load_b16(rs, soff, so1, 0);
+        r1.b = __builtin_amdgcn_raw_buffer_load_b16(rb, soff, so1, 0);
       }
     };
     // Redistribution after the WS loads. v_permlane16_swap exchanges lanes 16-31 of its
