@@ -23,6 +23,26 @@ thread_local std::string t_launches;  // this thread's kernel-choice record
 
 void launch_log_begin() { t_launches.clear(); }
 
+int device_compute_units() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+    (void)hipGetLastError();
+    return 256;
+  }
+  if (dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) {
+    (void)hipGetLastError();
+    cus = 256;
+  }
+  if (dev < 64) cache[dev].store(cus, std::memory_order_relaxed);
+  return cus;
+}
+
 void launch_log(dim3 grid, dim3 block, size_t lds_bytes, const char* fmt, ...) {
   char name[256];
   va_list ap;

@@ -18,6 +18,10 @@ void launch_log_begin();
 void launch_log(dim3 grid, dim3 block, size_t lds_bytes, const char* fmt, ...)
     __attribute__((format(printf, 4, 5)));
 
+// Compute units of the calling thread's current device (cached per device; 256 when
+// the query fails).
+int device_compute_units();
+
 // GEMV / small-M path: y[M, N] = x[M, K] * dequant(w)^T, rows taken 8 at a time.
 hipError_t launch_qmv(const uint16_t* x, const uint32_t* w, const uint16_t* scales,
                       const uint16_t* biases, void* y, int64_t M, int64_t N, int64_t K, int bits,

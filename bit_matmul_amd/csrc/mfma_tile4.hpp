@@ -86,10 +86,9 @@ struct MmTile4 {
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
   // Only the measured and tested depths: weights four groups ahead, activation copies two
   // groups ahead. Paired 4-bit loads six or eight groups ahead, and copies one group ahead
-  // (with 160-row tiles), once gave wrong results on the device. A model of the compiled
-  // loop (the issue order of its copies, weight loads, waits and barriers) finds every copy
-  // landed and every LDS read retired at each barrier for those variants too, so the copy
-  // bookkeeping below is not what failed; the cause was not found, and they stay disabled.
+  // (with 160-row tiles), once gave wrong results on the device, most likely from the
+  // miscount that vm_after_copy_tail removes (the last bodies' weight loads, unused, were
+  // dropped by the compiler while the waits still counted them); they stay disabled.
   static_assert(PD == 4 && XD == 2, "prefetch depths: only the tested PD = 4, XD = 2");
   static_assert(!WS || BITS == 8 || PD % 2 == 0, "paired weight loads");
   // Weight-side loads issued by body h: WL each, or with paired 4-bit loads 2 WL from odd
@@ -103,6 +102,13 @@ struct MmTile4 {
     for (int d = 0; d < XD; ++d) t += loads_of(I - d);
     return t;
   }
+  // The same for the last G % PD bodies, which issue no weight loads (their groups would
+  // lie past the end): after the copies of group g+1 come only the loads of the body
+  // before, when that is the last body of the unrolled loop, and this body's copies.
+  // Counts of loads that were never issued would let the wait pass early, so the tail
+  // issues none rather than relying on loads the compiler may drop as unused or merge
+  // (two clamped to the same last group read the same address).
+  static constexpr int vm_after_copy_tail(int I) { return (XD - 1) * XC + (I == 0 ? loads_of(PD - 1) : 0); }
   static_assert(PD * WL + XD * XC <= 63, "vmcnt range");
   static_assert(WAVES * BM * 64 <= NB * XB, "epilogue staging fits in the activation buffers");
 
@@ -404,8 +410,9 @@ struct MmTile4 {
     // step 0). Issues the activation copies of group g+XD and the weight loads of group
     // g+PD (into slot I, spent by then). Ends with the wait for the copies of group g+1
     // and the barrier.
-    auto body = [&](auto Ic, int g) {
+    auto body = [&](auto Ic, int g, auto Tc) {
       constexpr int I = decltype(Ic)::value;
+      constexpr bool TAIL = decltype(Tc)::value;  // one of the last G % PD bodies
       const Wraw& wc = wr[I];
       Wraw& wn = wr[(I + 1) % PD];
       uint32_t sn = 0, bn = 0;  // staged scale and bias of group g+1
@@ -444,7 +451,7 @@ struct MmTile4 {
           if (k * (3 * MB) / XC == p) copy_x(g + XD, xdst, k);
         // Weight loads of group g+PD once the codes of group g are spent (step 3); paired
         // 4-bit loads go out from odd bodies, for groups g+PD-1 and g+PD.
-        if (p == 3 * MB) {
+        if (!TAIL && p == 3 * MB) {
           if constexpr (WS && BITS == 4) {
             if constexpr (I % 2 == 1) load_pair(g + PD - 1, wr[(I + PD - 1) % PD], wr[I]);
           } else {
@@ -493,7 +500,7 @@ struct MmTile4 {
       acur = anext;
       // The copies of group g+1 (issued XD-1 bodies earlier) and everything before them
       // have landed; later copies and weight loads may still fly.
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(vm_after_copy(I)) : "memory");
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(TAIL ? vm_after_copy_tail(I) : vm_after_copy(I)) : "memory");
       barrier_no_fence();
     };
 
@@ -501,9 +508,10 @@ struct MmTile4 {
     // slot index is a constant; the last G % PD groups run one body each.
     int g = 0;
 #pragma unroll 1
-    for (; g + PD <= G; g += PD) static_for<0, PD>([&](auto Ic) { body(Ic, g + decltype(Ic)::value); });
+    for (; g + PD <= G; g += PD)
+      static_for<0, PD>([&](auto Ic) { body(Ic, g + decltype(Ic)::value, std::false_type{}); });
     static_for<0, PD - 1>([&](auto Ic) {
-      if (g + decltype(Ic)::value < G) body(Ic, g + decltype(Ic)::value);
+      if (g + decltype(Ic)::value < G) body(Ic, g + decltype(Ic)::value, std::true_type{});
     });
     // No copy may still be writing LDS when the workgroup moves on or ends, and no wave
     // reads the activation buffers any more once all have passed this barrier.

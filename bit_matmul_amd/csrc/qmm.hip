@@ -61,17 +61,48 @@ hipError_t launch_mb(QmmParams p, hipStream_t stream) {
                : launch_tiles<MmTile4<BITS, MB, 4, 4, 2, 0, 0, false, BITS != 2>>(p, stream);
 }
 
+// Row blocks per tile. Every tile reads all of K, so the choice trades the tile's own
+// speed (fewer rows: shorter loop bodies) against how many tiles the grid needs and
+// how many rounds of one tile per CU they take. Timed on the device at K = 5120, one
+// tile per CU, a tile of MB row blocks takes about (MB + 5.5) units (MB = 2: 36.5 us,
+// 4: 44, 6: 53, 8: 64, 10: 76); the grid's time is its rounds times that. The choice
+// minimises it, larger tiles first on ties (fewer re-reads of the weights). For each
+// candidate the row blocks are spread evenly over its number of row tiles. Measured
+// against one fixed choice: M = 600, K = 13824, N = 5120 (40 column tiles) 219 -> 139 us
+// (MB 10 -> 4), M = 600, N = 2048 76 -> 36.5 us (10 -> 2), M = 128, N = 13824 44 -> 38.5
+// us (4 -> 2); M = 600, N = 13824 keeps MB = 10 (85 us; 6 gives 110, 8 gives 128).
+int pick_row_blocks(int64_t M, int64_t N, int64_t cus) {
+  static constexpr int kMB[] = {10, 8, 6, 4, 2, 1};
+  const int64_t blocks = (M + 31) / 32;
+  const int64_t tiles_n = (N + 127) / 128;
+  int best = 10;
+  int64_t best_cost = -1;
+  for (const int mb : kMB) {
+    const int64_t tiles_m = (blocks + mb - 1) / mb;
+    const int64_t per = (blocks + tiles_m - 1) / tiles_m;  // row blocks of the fullest tile
+    int used = 10;
+    for (const int c : kMB)
+      if (c >= per) used = c;  // the smallest tile that holds them
+    const int64_t rounds = (tiles_m * tiles_n + cus - 1) / cus;
+    const int64_t cost = rounds * (2 * used + 11);
+    if (best_cost < 0 || cost < best_cost) {
+      best_cost = cost;
+      best = used;
+    }
+  }
+  return best;
+}
+
 template <int BITS>
 hipError_t launch_tile4(QmmParams p, hipStream_t stream) {
-  const int64_t blocks = (p.M + 31) / 32;
-  const int64_t tiles = (blocks + 9) / 10;
-  const int64_t per = (blocks + tiles - 1) / tiles;
-  if (per <= 1) return launch_mb<BITS, 1>(p, stream);
-  if (per <= 2) return launch_mb<BITS, 2>(p, stream);
-  if (per <= 4) return launch_mb<BITS, 4>(p, stream);
-  if (per <= 6) return launch_mb<BITS, 6>(p, stream);
-  if (per <= 8) return launch_mb<BITS, 8>(p, stream);
-  return launch_mb<BITS, 10>(p, stream);
+  switch (pick_row_blocks(p.M, p.N, device_compute_units())) {
+    case 1: return launch_mb<BITS, 1>(p, stream);
+    case 2: return launch_mb<BITS, 2>(p, stream);
+    case 4: return launch_mb<BITS, 4>(p, stream);
+    case 6: return launch_mb<BITS, 6>(p, stream);
+    case 8: return launch_mb<BITS, 8>(p, stream);
+    default: return launch_mb<BITS, 10>(p, stream);
+  }
 }
 
 }  // namespace

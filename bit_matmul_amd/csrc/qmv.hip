@@ -10,8 +10,6 @@
 //   qmv_kernel (qmv_impl.hpp): up to 8 activation rows per launch, any K (several
 //     passes over K when a row does not fit), for what the others do not take (2-bit
 //     codes with K past the split kernel's range: four rows per launch).
-#include <atomic>
-
 #include "kernels.hpp"
 #include "qmv_dma.hpp"
 #include "qmv_impl.hpp"
@@ -19,26 +17,6 @@
 #include "qmv_split.hpp"
 
 namespace bitmm {
-
-namespace {
-
-// Compute units of the current device (cached per device id).
-int compute_units() {
-  static std::atomic<int> cache[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
-  if (dev < 64) {
-    const int c = cache[dev].load(std::memory_order_relaxed);
-    if (c > 0) return c;
-  }
-  int cus = 0;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-    cus = 256;
-  if (dev < 64) cache[dev].store(cus, std::memory_order_relaxed);
-  return cus;
-}
-
-}  // namespace
 
 namespace {
 
@@ -64,9 +42,9 @@ hipError_t launch_rows(const uint16_t* x, const uint32_t* w, const uint16_t* sca
     dp.out_f32 = out_f32 ? 1 : 0;
     dp.steps_per_wave = dp.total_steps = 0;
     dp.bt = bt;
-    return bits == 4   ? qmv_dma_detail::launch_bits<4>(dp, compute_units(), 0, stream)
-           : bits == 2 ? qmv_dma_detail::launch_bits<2>(dp, compute_units(), 0, stream)
-                       : qmv_dma_detail::launch_bits<8>(dp, compute_units(), 0, stream);
+    return bits == 4   ? qmv_dma_detail::launch_bits<4>(dp, device_compute_units(), 0, stream)
+           : bits == 2 ? qmv_dma_detail::launch_bits<2>(dp, device_compute_units(), 0, stream)
+                       : qmv_dma_detail::launch_bits<8>(dp, device_compute_units(), 0, stream);
   }
   // Dense calls with several rows: the matrix-core GEMV, eight rows per launch.
   if (bt.exp == nullptr && M >= 2 && qmv_mfma_detail::fits(K, bits, M < 8 ? M : 8)) {
@@ -84,9 +62,9 @@ hipError_t launch_rows(const uint16_t* x, const uint32_t* w, const uint16_t* sca
       mp.out_f32 = out_f32 ? 1 : 0;
       mp.mask = 0x000F000Fu;
       mp.magic = 0x43004300u;
-      const hipError_t e = bits == 4   ? qmv_mfma_detail::launch_bits<4>(mp, compute_units(), stream)
-                           : bits == 2 ? qmv_mfma_detail::launch_bits<2>(mp, compute_units(), stream)
-                                       : qmv_mfma_detail::launch_bits<8>(mp, compute_units(), stream);
+      const hipError_t e = bits == 4   ? qmv_mfma_detail::launch_bits<4>(mp, device_compute_units(), stream)
+                           : bits == 2 ? qmv_mfma_detail::launch_bits<2>(mp, device_compute_units(), stream)
+                                       : qmv_mfma_detail::launch_bits<8>(mp, device_compute_units(), stream);
       if (e != hipSuccess) return e;
     }
     return hipSuccess;

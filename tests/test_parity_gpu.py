@@ -107,13 +107,48 @@ def test_qmm_small_m(M, N, K, bits, out):
 
 MFMA_SHAPES = [(8, 16, 64), (9, 100, 192), (16, 128, 128), (33, 70, 320), (130, 300, 576),
                (129, 257, 1024), (257, 129, 192), (200, 513, 448),
-               # row tiles of 32-row blocks: one group, two, three (one unrolled pass),
-               # four; a full 320-row tile, a ragged one, three row tiles
+               # K loops of one group, two, three (one unrolled pass), four; M at and
+               # just past a multiple of 320 rows, three times 320 and one row more
                (96, 40, 64), (300, 200, 128), (65, 1000, 704), (320, 128, 192),
                (321, 131, 256), (641, 96, 320),
                # scales and biases staged in LDS up to 80 groups (G even), fetched per
                # group beyond
                (100, 70, 5120), (70, 66, 5248)]
+
+
+# One shape for each row-tile size of the matrix-core GEMM (1, 2, 4, 6, 8 and 10 blocks
+# of 32 rows), each with a ragged last row tile and a ragged last column block. The
+# dispatch picks the size from M, N and the device's compute units; these shapes make
+# each pick on a 256-CU device, where the kernel-choice record is checked too. K = 192
+# fetches scales per group (odd group count), K = 128, 256 and 320 stage them in LDS.
+TILE_SHAPES = [(20, 130, 320, 1), (45, 16500, 128, 2), (250, 11000, 192, 4), (300, 11000, 256, 6),
+               (400, 13000, 192, 8), (577, 11111, 256, 10)]
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("M,N,K,mb", TILE_SHAPES)
+def test_qmm_mfma_each_row_tile(M, N, K, mb, bits):
+    d = I.random_dense(M, N, K, bits, seed=M + N + K + bits)
+    got = G.to_f64(G.run_dense("bitmm_qmm", d, "bf16"))
+    rec = bm.bitmm_last_launches()
+    if G.torch().cuda.get_device_properties(G.dev()).multi_processor_count == 256:
+        assert len(rec) == 1 and rec[0].startswith(f"qmm_mfma_kernel<MmTile4<{bits}, {mb}, "), rec
+    G.assert_close(got, oracle_dense(d), "bf16", f"qmm tile MB{mb} M{M} N{N} K{K} b{bits}")
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("M,N,K", [(257, 129, 192), (96, 128, 192), (300, 700, 704), (64, 129, 320)])
+def test_qmm_tail_bodies_wait_for_their_copies(M, N, K, bits):
+    """Regression: the K groups left after the unrolled loop of four (here 3, 3, 11 and 5
+    groups) run one body each with the activation copies of the next group landing
+    during the body before. With 32-row tiles a body is four MFMAs long, so a wait that
+    passes early shows as a few wrong rows; it did when the wait counted weight loads
+    that those bodies never issued. Several calls, since a race need not show in one."""
+    d = I.random_dense(M, N, K, bits, seed=M * N + K + bits)
+    ref = oracle_dense(d)
+    for rep in range(4):
+        got = G.to_f64(G.run_dense("bitmm_qmm", d, "bf16"))
+        G.assert_close(got, ref, "bf16", f"qmm tail M{M} N{N} K{K} b{bits} call {rep}")
 
 
 @pytest.mark.parametrize("bits", [4, 8])

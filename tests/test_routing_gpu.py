@@ -62,7 +62,9 @@ def test_qmv_routes(M, N, K, bits, want):
     (5, 4, "qmv_mfma_kernel<4, 2, 8, 2, 1, 2> "),   # two row groups
     (8, 4, "qmv_mfma_kernel<4, 2, 8, 2, 1, 2> "),   # M = 8 stays on the GEMV where it fits
     (9, 4, "qmm_mfma_kernel<MmTile4<4, 1, 4, 4, 2, 1, 80, false, true>> "),
-    (64, 4, "qmm_mfma_kernel<MmTile4<4, 2, 4, 4, 2, 1, 80, false, true>> "),
+    (64, 4, "qmm_mfma_kernel<MmTile4<4, 1, 4, 4, 2, 1, 80, false, true>> grid=216x1"),  # 2 x 108 tiles
+    (128, 4, "qmm_mfma_kernel<MmTile4<4, 2, 4, 4, 2, 1, 80, false, true>> grid=216x1"),
+    (300, 4, "qmm_mfma_kernel<MmTile4<4, 6, 4, 4, 2, 1, 80, false, true>> grid=216x1"),
     (600, 4, "qmm_mfma_kernel<MmTile4<4, 10, 4, 4, 2, 1, 80, false, true>> grid=216x1 block=256 lds=163840"),
     (600, 8, "qmm_mfma_kernel<MmTile4<8, 10, 4, 4, 2, 1, 80, false, true>> grid=216x1"),
     (600, 2, "qmm_mfma_kernel<MmTile4<2, 10, 4, 4, 2, 1, 80, false, false>> grid=216x1"),
@@ -70,6 +72,19 @@ def test_qmv_routes(M, N, K, bits, want):
 def test_qmm_routes_hidden5120(M, bits, want):
     r = one(dense("bitmm_qmm", M, 13824, 5120, bits))
     assert r.startswith(want), r
+
+
+@pytest.mark.parametrize("M,N,K,want", [
+    # Narrow N: smaller row tiles, so that the grid fills the CUs in one round
+    (600, 5120, 13824, "qmm_mfma_kernel<MmTile4<4, 4, 4, 4, 2, 0, 0, false, true>> grid=200x1"),
+    (600, 5120, 5120, "qmm_mfma_kernel<MmTile4<4, 4, 4, 4, 2, 1, 80, false, true>> grid=200x1"),
+    (600, 2048, 5120, "qmm_mfma_kernel<MmTile4<4, 2, 4, 4, 2, 1, 80, false, true>> grid=160x1"),
+    (600, 700, 512, "qmm_mfma_kernel<MmTile4<4, 1, 4, 4, 2, 1, 80, false, true>> grid=114x1"),
+    # Large M: rounds of 256 tiles; 2048 rows at N = 5120 in 11 tiles of 192 rows
+    (2048, 5120, 5120, "qmm_mfma_kernel<MmTile4<4, 6, 4, 4, 2, 1, 80, false, true>> grid=440x1"),
+])
+def test_qmm_row_tile_choice(M, N, K, want):
+    assert one(dense("bitmm_qmm", M, N, K, 4)).startswith(want)
 
 
 def test_qmm_group32_loads_scales_per_group():
