@@ -26,8 +26,8 @@ Also reported:
       counter figures and the traced-vs-untraced reconciliation from the committed
       rocprofv3 summaries under ``profiles/`` when they were taken on these kernel
       sources.
-  ``measured_ceilings``: a plain streaming read of 40 MB, 160 MB and 1 GiB in the
-      decode GEMV's access shape, and a loop of independent bf16 matrix-core
+  ``measured_ceilings``: a plain streaming read of 8, 16, 40 and 160 MiB and 1 GiB in
+      the decode GEMV's access shape, timed by graph replay like the workloads, and a loop of independent bf16 matrix-core
       instructions (``libbitmm_probe.so``): what this chip reaches, beside the
       published peaks.
   ``cpu_baseline``: the CPU oracle on the host cores, whole headline steps for about
@@ -393,31 +393,35 @@ def measured_ceilings(torch):
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream().cuda_stream
     out = {"read_GB_s": {}, "read_unroll": {}}
-    for size in (40 << 20, 160 << 20, 1 << 30):
+
+    class _Read:
+        """One probe read per launch, rotating through the buffers (on the stream current at
+        launch time, so that it can be captured)."""
+
+        def __init__(self, bufs, size, unroll, sink):
+            self.bufs, self.size, self.unroll, self.sink, self.i = bufs, size, unroll, sink, 0
+
+        def launch(self):
+            b = self.bufs[self.i % len(self.bufs)]
+            self.i += 1
+            rc = L.bitmm_probe_stream_read(b.data_ptr(), self.size, self.unroll, self.sink.data_ptr(),
+                                           torch.cuda.current_stream().cuda_stream)
+            if rc != 0:
+                raise RuntimeError(f"stream read probe failed ({rc})")
+
+    # Sizes around every workload's bytes (the MoE decode's 9 MB, the N = 5120 GEMV's 15 MB,
+    # the headline's 40 MB, the grouped GEMMs' 175 MB, the dense grouped product's 0.5 GB).
+    for size in (8 << 20, 16 << 20, 40 << 20, 160 << 20, 1 << 30):
         copies = max(2, -(-ROTATE_BYTES // size)) if size < ROTATE_BYTES else 2
         bufs = [torch.ones(size, dtype=torch.uint8, device=dev) for _ in range(copies)]
         best = None
         for unroll in (4, 8, 16):
             sink = torch.empty(int(L.bitmm_probe_stream_read_sink_words(size, unroll)), dtype=torch.int32,
                                device=dev)
-            reps = 20 if size < (1 << 30) else 6
-
-            def run(i):
-                rc = L.bitmm_probe_stream_read(bufs[i % copies].data_ptr(), size, unroll, sink.data_ptr(),
-                                               stream)
-                if rc != 0:
-                    raise RuntimeError(f"stream read probe failed ({rc})")
-            for i in range(copies):
-                run(i)
-            torch.cuda.synchronize()
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record()
-            for i in range(reps):
-                run(i)
-            e1.record()
-            torch.cuda.synchronize()
-            gbs = size * reps / (e0.elapsed_time(e1) / 1e3) / 1e9
+            steps = max(copies, 20) if size < (1 << 30) else 6
+            # timed like the workloads: the reads captured into one graph, replayed
+            secs = time_steps(torch, [_Read(bufs, size, unroll, sink)], steps, copies, repeats=3)
+            gbs = size * steps / sorted(secs)[1] / 1e9
             if best is None or gbs > best[0]:
                 best = (gbs, unroll)
         out["read_GB_s"][str(size)] = round(best[0], 1)
@@ -440,7 +444,8 @@ def measured_ceilings(torch):
     out["mfma_bf16_TFLOP_s"] = round(tflops, 1)
     out["mfma_probe"] = f"{waves} waves x {iters} x 8 independent v_mfma_f32_32x32x16_bf16"
     out["read_probe"] = ("one pass over the buffer, each wave instruction 1 KB contiguous, all loads of a wave "
-                         "issued before use; best of 4, 8, 16 KB per wave; copies rotate through >= 1 GiB")
+                         "issued before use; best of 4, 8, 16 KB per wave; copies rotate through >= 1 GiB; "
+                         "timed by graph replay like the workloads, middle of 3 replays")
     log(f"ceiling: bf16 matrix cores {tflops:.1f} TFLOP/s")
     return out
 
