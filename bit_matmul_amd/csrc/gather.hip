@@ -22,6 +22,7 @@ namespace bitmm {
 namespace {
 
 constexpr int kPrepThreads = 1024;
+constexpr int kPrepRun = 8;  // rows per thread whose ids are loaded together
 
 // ws[0]: 0 if the ids are valid, else 1 + first offending row.
 // ws[1 + e], e in [0, E]: first row whose id is >= e (row offsets of the experts).
@@ -40,14 +41,29 @@ __global__ __launch_bounds__(kPrepThreads) void gather_prepare_kernel(const int3
   __syncthreads();
   int32_t* off = reinterpret_cast<int32_t*>(ws + 1);
   int mine = B;
-  for (int r = threadIdx.x; r < B; r += kPrepThreads) {
-    const int c = idx[r];
-    const int a = r > 0 ? idx[r - 1] : -1;
-    if (c < 0 || c >= E || a > c) {
-      mine = min(mine, r);
-      continue;
+  // kPrepRun rows per thread and pass, all their ids loaded before any is used: one
+  // memory latency per pass instead of one per row.
+  for (int base = 0; base < B; base += kPrepThreads * kPrepRun) {
+    int cv[kPrepRun], av[kPrepRun];
+    // Unconditional loads (rows past the end re-read the last one and are not used): a
+    // load under a condition would be waited for where the paths join.
+#pragma unroll
+    for (int k = 0; k < kPrepRun; ++k) {
+      const int r = min(base + (int)threadIdx.x + k * kPrepThreads, B - 1);
+      cv[k] = idx[r];
+      av[k] = idx[max(r - 1, 0)];
     }
-    for (int e = max(a, -1) + 1; e <= c; ++e) off[e] = r;  // a may be an invalid id
+#pragma unroll
+    for (int k = 0; k < kPrepRun; ++k) {
+      const int r = base + (int)threadIdx.x + k * kPrepThreads;
+      if (r >= B) break;
+      const int c = cv[k], a = r > 0 ? av[k] : -1;
+      if (c < 0 || c >= E || a > c) {
+        mine = min(mine, r);
+        continue;
+      }
+      for (int e = max(a, -1) + 1; e <= c; ++e) off[e] = r;  // a may be an invalid id
+    }
   }
   if (B > 0 && threadIdx.x == 0) {
     const int last = idx[B - 1];
@@ -120,12 +136,35 @@ __global__ __launch_bounds__(kPrepThreads) void gather_sort_kernel(const int32_t
   if (threadIdx.x == 0) first_bad = B;
   __syncthreads();
   int mine = B;
-  for (int r = threadIdx.x; r < B; r += kPrepThreads) {
-    const int e = exp[r];
-    const int t = tok ? tok[r] : r;
-    const bool ok = e >= 0 && e < E && t >= 0 && t < T;
-    atomicAdd(&cnt[ok ? e : E], 1);
-    if (!ok) mine = min(mine, r);
+  // Expert and token ids of kPrepRun rows per thread, loaded before any is used (one
+  // memory latency per pass); with one pass they stay in registers for the second loop.
+  int ev[kPrepRun], tv[kPrepRun];
+  // Unconditional loads (rows past the end re-read the last one and are not used), the
+  // token test outside the unrolled loop: a load under a condition would be waited for
+  // where the paths join.
+  auto load_ids = [&](int base) {
+#pragma unroll
+    for (int k = 0; k < kPrepRun; ++k) ev[k] = exp[min(base + (int)threadIdx.x + k * kPrepThreads, B - 1)];
+    if (tok) {
+#pragma unroll
+      for (int k = 0; k < kPrepRun; ++k) tv[k] = tok[min(base + (int)threadIdx.x + k * kPrepThreads, B - 1)];
+    } else {
+#pragma unroll
+      for (int k = 0; k < kPrepRun; ++k) tv[k] = base + (int)threadIdx.x + k * kPrepThreads;
+    }
+  };
+  const bool one_pass = B <= kPrepThreads * kPrepRun;
+  for (int base = 0; base < B; base += kPrepThreads * kPrepRun) {
+    load_ids(base);
+#pragma unroll
+    for (int k = 0; k < kPrepRun; ++k) {
+      const int r = base + (int)threadIdx.x + k * kPrepThreads;
+      if (r >= B) break;
+      const int e = ev[k], t = tv[k];
+      const bool ok = e >= 0 && e < E && t >= 0 && t < T;
+      atomicAdd(&cnt[ok ? e : E], 1);
+      if (!ok) mine = min(mine, r);
+    }
   }
   if (mine < B) atomicMin(&first_bad, mine);
   __syncthreads();
@@ -134,17 +173,22 @@ __global__ __launch_bounds__(kPrepThreads) void gather_sort_kernel(const int32_t
   int32_t* perm = reinterpret_cast<int32_t*>(ws + 2 + E);
   for (int e = threadIdx.x; e <= E; e += kPrepThreads) off[e] = cnt[e];
   __syncthreads();
-  for (int r = threadIdx.x; r < B; r += kPrepThreads) {
-    const int e = exp[r];
-    const int t = tok ? tok[r] : r;
-    const bool ok = e >= 0 && e < E && t >= 0 && t < T;
-    perm[atomicAdd(&cnt[ok ? e : E], 1)] = r;
-    if (!ok) {
-      for (int n = 0; n < N; ++n) {
-        if (ysz == 4)
-          static_cast<uint32_t*>(y)[(int64_t)r * N + n] = 0u;
-        else
-          static_cast<uint16_t*>(y)[(int64_t)r * N + n] = 0;
+  for (int base = 0; base < B; base += kPrepThreads * kPrepRun) {
+    if (!one_pass) load_ids(base);
+#pragma unroll
+    for (int k = 0; k < kPrepRun; ++k) {
+      const int r = base + (int)threadIdx.x + k * kPrepThreads;
+      if (r >= B) break;
+      const int e = ev[k], t = tv[k];
+      const bool ok = e >= 0 && e < E && t >= 0 && t < T;
+      perm[atomicAdd(&cnt[ok ? e : E], 1)] = r;
+      if (!ok) {
+        for (int n = 0; n < N; ++n) {
+          if (ysz == 4)
+            static_cast<uint32_t*>(y)[(int64_t)r * N + n] = 0u;
+          else
+            static_cast<uint16_t*>(y)[(int64_t)r * N + n] = 0;
+        }
       }
     }
   }
