@@ -42,11 +42,15 @@ Profiling helpers (no GPU needed for the second):
       ``bitmm:<workload>`` (for ``rocprofv3 --marker-trace``).
   ``--summarize DIR``: read the rocprofv3 CSV output under DIR and print the summary
       text kept under ``profiles/`` (kernel statistics, per-workload kernel time per
-      launch from the markers, counter figures per kernel).
+      launch from the markers, counter figures per kernel). ``--bench-json`` names the
+      untraced bench line of the same session, ``--workload`` takes the algorithmic
+      bytes of one of its workloads for the traffic ratio, ``--title`` and ``--command``
+      head the text. Every file under ``profiles/`` is this output, redirected.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--repeats R] [--no-suite]
                        [--no-cpu] [--no-ceilings] [--calibrate-copy] [--only NAMES]
-                       [--markers] [--summarize DIR [--bench-json FILE] [--command CMD]]
+                       [--markers] [--summarize DIR [--bench-json FILE] [--workload NAME]
+                                                    [--title TEXT] [--command CMD]]
 """
 
 from __future__ import annotations
@@ -655,13 +659,41 @@ def summarize_counters(files, algorithmic_bytes=None):
     return out
 
 
+def workload_bytes(bench_json: str, workload: str) -> int:
+    """Algorithmic bytes per launch of `workload` in an untraced bench line."""
+    with open(bench_json) as f:
+        for line in f:
+            line = line.strip()
+            if line.startswith("{"):
+                j = json.loads(line)
+                for e in j.get("suite", []) + j.get("per_kernel", []):
+                    if e["workload"] == workload:
+                        return int(e["bytes"])
+    raise SystemExit(f"{workload}: not in {bench_json}")
+
+
 def summarize_profile(d: str, bench_json: str | None, command: str | None,
-                      algorithmic_bytes: int | None = None) -> str:
+                      algorithmic_bytes: int | None = None, title: str | None = None,
+                      argv: list | None = None) -> str:
     """Text summary of the rocprofv3 CSV output under d (searched recursively)."""
     out = []
     src_hash = kernel_sources_hash()
+    if title:
+        out.append(f"# {title}")
+    if argv:
+        # how this text was made (the rocprofv3 command is the line below)
+        shown, skip = [], False
+        for a in argv:
+            if skip:
+                shown.append("CMD")
+                skip = False
+                continue
+            shown.append(a if (a.replace("/", "").replace("_", "").replace("-", "").replace(".", "").isalnum())
+                         else json.dumps(a))
+            skip = a == "--command"
+        out.append("# summarised by: python3 bench.py " + " ".join(shown))
     if command:
-        out.append("# command (repository root, GPU box; cd /tmp && export TMPDIR=/tmp first):")
+        out.append("# command (from the repository root on the MI355X host; cd /tmp && export TMPDIR=/tmp first):")
         out.append(f"#   {command}")
     out.append(f"kernel_sources_sha256_16: {src_hash}")
     traces = sorted(glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True))
@@ -747,13 +779,20 @@ def main():
     ap.add_argument("--bench-json", default=None)
     ap.add_argument("--command", default=None)
     ap.add_argument("--algorithmic-bytes", type=int, default=None)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--title", default=None)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a 256 MiB device-to-device copy 5 times: the reference "
                          "for scaling the FETCH_SIZE / WRITE_SIZE counters to bytes")
     args = ap.parse_args()
     if args.summarize:
-        sys.stdout.write(summarize_profile(args.summarize, args.bench_json, args.command,
-                                           args.algorithmic_bytes))
+        nbytes = args.algorithmic_bytes
+        if args.workload:
+            if not args.bench_json:
+                raise SystemExit("--workload needs --bench-json")
+            nbytes = workload_bytes(args.bench_json, args.workload)
+        sys.stdout.write(summarize_profile(args.summarize, args.bench_json, args.command, nbytes,
+                                           args.title, sys.argv[1:]))
         return
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
