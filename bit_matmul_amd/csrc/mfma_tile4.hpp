@@ -20,8 +20,9 @@
 //   * Activations are the only operand staged in LDS (three buffers of one group, BM rows
 //     x 128 bytes, copied HBM -> LDS without passing through registers, two groups ahead).
 //     One barrier per group.
-//   * Buffer descriptors are formed once; only scalar offsets move with the group. The
-//     loop body is unrolled three times so every LDS buffer index is a constant.
+//   * Buffer descriptors are formed once; only scalar offsets move with the group (the
+//     group's LDS buffer too). The loop body is unrolled PD times so every slot of the
+//     weight ring is a constant register index.
 //
 // K order within a group (a contraction, so any order that pairs x and w alike is exact):
 // MFMA k-step u (0..3) gives k-slot 8h + i of lane (c, h) code 32h + 8u + i of the group,

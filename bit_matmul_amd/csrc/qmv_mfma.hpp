@@ -17,9 +17,10 @@
 // workgroup: wave w owns chunks 16 C w .. 16 C (w + 1) - 1 and lane (b, i) the chunks
 // 16 C w + b + 16 j, j < C (so one load instruction of a wave reads four weight rows x
 // 256 contiguous bytes). The activations of those chunks stay in registers for the
-// whole kernel. A workgroup computes SPW steps of four consecutive weight rows; every
-// load of all of its steps is issued before any arithmetic (straight-line code, so the
-// compiler's wait counts are exact). The scales and biases of the workgroup's rows, one
+// whole kernel. A workgroup computes SPW steps of four consecutive weight rows, and each
+// wave keeps the loads of D steps in flight: those of step i + D go out as soon as step
+// i has been computed and its registers are free (straight-line code, so the compiler's
+// wait counts are exact). The scales and biases of the workgroup's rows, one
 // contiguous span of each array, are copied into LDS at the start by a few coalesced
 // direct-to-LDS loads (the lanes of one MFMA block read four different rows, so loading
 // them per lane cost a third of the kernel's time). Per step the 16 blocks' partial sums of each row
