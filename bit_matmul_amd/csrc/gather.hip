@@ -195,6 +195,42 @@ __global__ __launch_bounds__(kPrepThreads) void gather_sort_kernel(const int32_t
   if (threadIdx.x == 0) ws[0] = first_bad < B ? (uint32_t)first_bad + 1u : 0u;
 }
 
+template <typename T>
+struct Tile {
+  using type = T;
+};
+
+// Calls f(Tile<U>{}, r0, rows) over the rows [r_begin, r_end) of one expert: once with a
+// tile of 32 or 64 rows when that holds them all and is smaller than T (the MFMAs then
+// skip the padding of a short expert), else with T over as many row tiles as the rows
+// need, LDS reused between them. The choice is uniform across the workgroup. With
+// about 36 rows per expert, a quarter of the experts have 32 rows or fewer: MoE up
+// 54.1 -> 52.6 us, down 59.2 -> 57.9, indexed form 55.2 -> 53.8 and 60.8 -> 59.7 (one
+// box, same session). Results are bit-identical: a row block's sums do not depend on
+// the tile's height.
+template <typename T, typename F>
+__device__ __forceinline__ void over_expert_rows(int r_begin, int r_end, F&& f) {
+  const int n = r_end - r_begin;
+  if constexpr (T::BM > 32) {
+    static_assert(T::template WithMB<1>::LDS_BYTES <= T::LDS_BYTES, "LDS of the shorter tile");
+    if (n <= 32) {
+      f(Tile<typename T::template WithMB<1>>{}, r_begin, n);
+      return;
+    }
+  }
+  if constexpr (T::BM > 64) {
+    static_assert(T::template WithMB<2>::LDS_BYTES <= T::LDS_BYTES, "LDS of the shorter tile");
+    if (n <= 64) {
+      f(Tile<typename T::template WithMB<2>>{}, r_begin, n);
+      return;
+    }
+  }
+  for (int r0 = r_begin; r0 < r_end; r0 += T::BM) {
+    if (r0 > r_begin) __syncthreads();  // LDS is reused by the next row block
+    f(Tile<T>{}, r0, min(T::BM, r_end - r0));
+  }
+}
+
 struct GatherParams {
   const uint16_t* x;
   const uint32_t* w;
@@ -246,12 +282,11 @@ __global__ __launch_bounds__(T::THREADS) void gather_qmm_kernel(GatherParams p) 
   const uint32_t* we = p.w + (int64_t)e * p.N * words;
   const uint16_t* se = p.s + (int64_t)e * p.N * groups;
   const uint16_t* be = p.b + (int64_t)e * p.N * groups;
-  for (int r0 = r_begin; r0 < r_end; r0 += T::BM) {
-    if (r0 > r_begin) __syncthreads();  // LDS is reused by the next row block
-    const int rows = min(T::BM, r_end - r0);
-    T::run(p.x + (int64_t)r0 * p.K, rows, we, se, be, n0, p.N, p.K, p.group,
+  over_expert_rows<T>(r_begin, r_end, [&](auto tile, int r0, int rows) {
+    using U = typename decltype(tile)::type;
+    U::run(p.x + (int64_t)r0 * p.K, rows, we, se, be, n0, p.N, p.K, p.group,
            static_cast<char*>(p.y) + (size_t)r0 * p.N * ysz, p.out_f32 != 0, lds);
-  }
+  });
 }
 
 // Indexed form: the rows of expert e are perm[off[e] .. off[e+1]); the tile gathers
@@ -273,12 +308,10 @@ __global__ __launch_bounds__(T::THREADS) void gather_qmm_indexed_kernel(GatherPa
   const uint32_t* we = p.w + (int64_t)e * p.N * words;
   const uint16_t* se = p.s + (int64_t)e * p.N * groups;
   const uint16_t* be = p.b + (int64_t)e * p.N * groups;
-  for (int r0 = r_begin; r0 < r_end; r0 += T::BM) {
-    if (r0 > r_begin) __syncthreads();  // LDS is reused by the next row block
-    const int rows = min(T::BM, r_end - r0);
-    T::run(p.x, rows, we, se, be, n0, p.N, p.K, p.group, p.y, p.out_f32 != 0, lds, perm + r0, p.tok,
-           p.T);
-  }
+  over_expert_rows<T>(r_begin, r_end, [&](auto tile, int r0, int rows) {
+    using U = typename decltype(tile)::type;
+    U::run(p.x, rows, we, se, be, n0, p.N, p.K, p.group, p.y, p.out_f32 != 0, lds, perm + r0, p.tok, p.T);
+  });
 }
 
 template <int BITS, typename T>
@@ -330,7 +363,8 @@ hipError_t launch_sb(GatherParams p, hipStream_t stream) {
 
 // One row of 4 waves, each with 32 weight rows: every expert's weights are dequantized
 // once per column block. Row blocks of 32 per tile from the mean rows per expert, with
-// slack for the spread of the routing; experts with more rows loop over row tiles.
+// slack for the spread of the routing; experts with more rows loop over row tiles, and
+// experts with fewer run a shorter tile (over_expert_rows).
 template <int BITS, bool RMAP>
 hipError_t launch_tile4(GatherParams p, hipStream_t stream) {
   const int64_t mean = p.E > 0 ? (p.B + p.E - 1) / p.E : p.B;

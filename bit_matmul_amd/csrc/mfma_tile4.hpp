@@ -62,6 +62,10 @@ namespace bitmm {
 template <int BITS, int MB, int WN, int PD = 3, int XD = 2, int SBM = 0, int GMAX = 0, bool RMAP = false,
           bool WS = false>
 struct MmTile4 {
+  // The same tile with M2 row blocks: a caller whose row count varies at run time (the
+  // grouped GEMMs, per expert) runs the smallest one that holds the rows.
+  template <int M2>
+  using WithMB = MmTile4<BITS, M2, WN, PD, XD, SBM, GMAX, RMAP, WS>;
   static constexpr int WAVES = WN;
   static constexpr int THREADS = 64 * WAVES;
   static constexpr int BM = 32 * MB;
@@ -150,7 +154,9 @@ struct MmTile4 {
     float s, b0, s16, b1;
   };
 
-  __device__ static void run(const uint16_t* __restrict__ x_rows_in, int rows_in,
+  // Always inlined: a kernel that runs tiles of two sizes would otherwise call them as
+  // functions, whose calling convention costs it about 45 registers.
+  __device__ __forceinline__ static void run(const uint16_t* __restrict__ x_rows_in, int rows_in,
                              const uint32_t* __restrict__ w_in, const uint16_t* __restrict__ sc_in,
                              const uint16_t* __restrict__ bi_in, int n0_in, int N, int K,
                              int group, void* __restrict__ y_rows, bool out_f32, char* lds,

@@ -188,6 +188,12 @@ GATHER_COUNTS = [
     [0, 0, 9],                            # leading empty experts
     [40] * 6,
     [3, 129, 0, 1],                       # a segment spanning three row blocks
+    # 64-row launch (mean 30 rows): experts of 5 and 32 rows run the 32-row tile, 33 and
+    # 37 the launch's, 70 two row tiles
+    [37, 0, 5, 70, 33, 32],
+    # 128-row launch (mean 64 rows): 10 rows the 32-row tile, 33, 50 and 64 the 64-row
+    # tile, 65, 100 and 120 the launch's, 129 two row tiles
+    [100, 10, 50, 0, 120, 33, 64, 65, 129],
 ]
 
 
